@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of one attention layer's engine step on one MI355X.
+
+A timed step is the whole hot path over one synthetic batch:
+  a1  C++ FIFO builder step (on a fresh copy of the prepared builder state),
+  a2  one packed async upload of the step descriptor,
+  a3  cb_kv_append of the step's K/V rows,
+  a4-a7  cb_attention_step (plan, the ragged decode+prefill kernel, split-K
+      combine, bf16 output).
+The default workload is the mixed step: 64 decode sequences (context uniform
+on [256, 8192]) plus prefill chunks 476 (at offset 1024), 700 and 808 of
+three prompts under max_batch_tokens = 2048; 32 query / 8 KV heads, head_dim
+128, bf16, 16-token pages.  ``--workload`` selects the other shapes.
+
+Prints ONE JSON line on stdout: query tokens/s, ms per step, the roofline of
+the main attention kernel (its duration measured with HIP events recorded on
+its stream around each launch), and the CPU oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+METRIC = "query tokens/s per mixed attention step + % of HBM/MFMA roofline, 1 MI355X"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload(name):
+    import workloads as wl
+    if name == "mixed":
+        return wl.mixed(), 0
+    if name == "decode":
+        return wl.decode_only(), 0
+    if name == "long":
+        return wl.long_prompt(), 38          # the heaviest 512-token chunk (offset 19456)
+    if name == "chunk":
+        w = wl.long_prompt()
+        w.requests = [r for r in w.requests if r[2] == 0]     # the long prompt alone
+        w.name = "longprompt_chunk_only_512@19456_gqa64/8_d128_bf16"
+        return w, 38
+    raise SystemExit(f"unknown workload {name}")
+
+
+def algorithmic(desc, hq, hkv, d, esize):
+    """Bytes the step must move and flops it must do (no padding, no re-reads)."""
+    import numpy as np
+    ctx = desc.context_lens.astype(np.int64)
+    ql = desc.q_lens.astype(np.int64)
+    off = ctx - ql
+    kv = int((ctx * 2 * hkv * d * esize).sum())
+    qo = int(2 * desc.num_tokens * hq * d * esize)
+    meta = int((-(-ctx // 16)).sum() * 4 + (3 * desc.num_seqs + 1) * 4)
+    pairs = ql * off + ql * (ql + 1) // 2
+    flops = int((4 * d * hq * pairs).sum())
+    return kv + qo + meta, flops, int(pairs.sum())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed", choices=["mixed", "decode", "long", "chunk"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention step shards by sequence or KV head with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_prefill_attention_amd as cb
+    from chunked_prefill_attention_amd.engine import PagedAttentionLayer
+    import workloads as wl
+
+    cb.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w, advance = workload(args.workload)
+    hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+    t_setup = time.perf_counter()
+    layer = PagedAttentionLayer(hq, hkv, d, w.pool_pages, w.max_batch_tokens, w.max_requests, w.dtype,
+                                w.max_prefill_chunk, w.safety_margin, page_shuffle_seed=w.seed, device=dev)
+    hist = {}
+    for i, (p, o, c) in enumerate(w.requests):
+        layer.builder.submit(i, p, o, c)
+    # K/V histories drawn on the device, per request (exact bf16 values)
+    for i, (p, o, c) in enumerate(w.requests):
+        n = p + o - 1
+        k = wl.device_normal((n, hkv, d), w.dtype, dev, w.seed, i, 1)
+        v = wl.device_normal((n, hkv, d), w.dtype, dev, w.seed, i, 2)
+        hist[i] = (k, v)
+        if c > 0:
+            layer.write_positions(layer.builder.block_table(i), 0, c, k[:c], v[:c])
+    for _ in range(advance):                       # earlier steps: append only
+        desc = layer.schedule()
+        meta = layer.upload(desc)
+        ks = torch.cat([hist[int(r)][0][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
+        vs = torch.cat([hist[int(r)][1][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
+        cb.kv_append(ks, vs, layer.k_cache, layer.v_cache, meta.slot_mapping)
+    base = layer.builder
+    clones = [base.clone() for _ in range(args.warmup + args.steps + 1)]
+    probe = clones.pop()
+    desc0 = probe.step()
+    T = desc0.num_tokens
+    q = wl.device_normal((T, hq, d), w.dtype, dev, w.seed, 99, 3)
+    kn = torch.cat([hist[int(r)][0][a:e] for r, a, e in zip(desc0.req_ids, desc0.q_offsets, desc0.context_lens)])
+    vn = torch.cat([hist[int(r)][1][a:e] for r, a, e in zip(desc0.req_ids, desc0.q_offsets, desc0.context_lens)])
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: setup {time.perf_counter() - t_setup:.1f}s; step: {desc0.num_seqs} seqs, "
+        f"{desc0.num_decodes} decodes, {T} query tokens, max ctx {desc0.max_context_len}")
+
+    esize = 2 if w.dtype == "bf16" else 4
+    bytes_alg, flops_alg, pairs = algorithmic(desc0, hq, hkv, d, esize)
+    lib = cb.load()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops:
+        e.record()
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(builder, k=None):
+        desc = builder.step()                                  # a1
+        meta = layer.upload(desc, stream=stream)               # a2
+        if k is not None:
+            lib.cb_profile_events(starts[k].cuda_event, stops[k].cuda_event)
+        layer.forward(meta, q, kn, vn, out=out, stream=stream)  # a3 .. a7
+        if k is not None:
+            lib.cb_profile_events(None, None)
+        return desc
+
+    for i in range(args.warmup):
+        one_step(clones[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(clones[args.warmup + k], k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
+    kern_s = float(np.mean(kern_ms)) / 1e3
+    assert torch.isfinite(out.float()).all(), "non-finite attention output"
+
+    t_hbm, t_mfma = bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(bytes_alg / kern_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(bytes_alg / kern_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops_alg / kern_s / 1e12, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(flops_alg / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "attn_mixed_kernel<128>" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel<128>"
+    roof["kernel_us"] = round(kern_s * 1e6, 2)
+    roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
+    log(f"[bench] step {step_s * 1e3:.3f} ms, attention kernel {kern_s * 1e6:.1f} us, "
+        f"{bytes_alg / 1e9:.3f} GB algorithmic, {flops_alg / 1e9:.1f} GFLOP")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(desc0, q, hist, hq, hkv, d, args.cpu_seconds, out)
+
+    rec = {
+        "metric": METRIC, "value": round(T / step_s, 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
+        "config": {"workload": w.name, "num_seqs": desc0.num_seqs, "num_decodes": desc0.num_decodes,
+                   "num_tokens": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "page_size": 16,
+                   "max_batch_tokens": w.max_batch_tokens, "max_context_len": desc0.max_context_len,
+                   "kv_bytes_read": bytes_alg, "visible_pairs": pairs, "flops": flops_alg},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(desc, q, hist, hq, hkv, d, budget_s, gpu_out):
+    """Time the fp64 oracle on the step's sequences (test infrastructure)."""
+    import numpy as np
+    from oracle import attention as ora
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] + [1])
+        blas_name = blas[0].get("internal_api", "?") if blas else "none"
+    except Exception:  # pragma: no cover
+        threads, blas_name = 1, "?"
+    import workloads as wl
+    scale = wl.softmax_scale(d)
+    qh = q.float().cpu().numpy()
+    gh = gpu_out.float().cpu().numpy()
+    seqs = []
+    for s in range(desc.num_seqs):
+        i = int(desc.req_ids[s])
+        c = int(desc.context_lens[s])
+        a, e = int(desc.query_start_loc[s]), int(desc.query_start_loc[s + 1])
+        seqs.append((qh[a:e], hist[i][0][:c].float().cpu().numpy(), hist[i][1][:c].float().cpu().numpy(), a, e))
+    tokens, t_used, reps, worst = 0, 0.0, 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        for qq, kk, vv, a, e in seqs:
+            ref = ora.attend(qq, kk, vv, scale)
+            if reps == 0:
+                worst = max(worst, float(np.abs(ref - gh[a:e]).max()))
+        t_used += time.perf_counter() - t0
+        tokens += desc.num_tokens
+        reps += 1
+        if t_used >= budget_s or reps >= 50:
+            break
+    log(f"[bench] cpu oracle: {reps} x whole step in {t_used:.1f}s ({threads} BLAS threads, {blas_name}); "
+        f"max |gpu - oracle| {worst:.3e}")
+    return {"value": round(tokens / t_used, 1), "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole step ({desc.num_tokens} query tokens, {desc.num_seqs} sequences), "
+                      f"{reps} repetition(s), fp64 numpy, {blas_name} BLAS",
+            "max_abs_err_vs_gpu": worst}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,333 @@
+// FIFO batch builder: the host half of one continuous-batching engine step.
+//
+// Hugging Face transformers, "Continuous batching architecture": sections
+// "Request lifecycle", "Chunked prefill", "Scheduler", "FIFO", "Admission".
+// Ultralytics glossary, "Chunked Prefill", "How chunked prefill works": one
+// token per running decode first, then prompt chunks fill the budget.
+// AI Engineering from Scratch, "vLLM serving internals", "What the scheduler
+// looks like": release finished requests, admit from the head of the waiting
+// queue while blocks are free, then batch decode tokens and prefill chunks.
+//
+// Per step the builder walks its live requests once (O(requests + new pages))
+// and writes the ragged descriptor into arrays it owns, ready to be copied to
+// the device in one go.  Pages come from a LIFO free list of physical ids.
+#include <algorithm>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "cb_internal.h"
+
+namespace {
+
+enum class State : int { Waiting, Prefilling, Decoding, Finished };
+
+struct Request {
+  int64_t id;
+  int32_t prompt_len;
+  int32_t output_len;
+  int64_t arrival;
+  int32_t cached = 0;     // tokens whose K/V is in the cache
+  int32_t generated = 0;  // output tokens produced so far
+  State state = State::Waiting;
+  std::vector<int32_t> pages;  // block table, logical order
+};
+
+uint64_t splitmix64(uint64_t& x) {
+  uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+struct cb_builder {
+  cb_builder_config cfg{};
+  std::vector<int32_t> free_list;       // stack; back() is handed out next
+  std::vector<std::unique_ptr<Request>> reqs;  // arrival order
+  std::unordered_map<int64_t, Request*> by_id;
+  int64_t arrivals = 0;
+  int64_t steps = 0;
+  int64_t total_stalls = 0;
+  int64_t total_finished = 0;
+
+  // step outputs (owned, valid until the next step)
+  std::vector<int64_t> o_req_ids, o_finished, o_stalled;
+  std::vector<int32_t> o_qsl, o_ctx, o_off, o_bt, o_slots;
+
+  int32_t take_page() {
+    int32_t p = free_list.back();
+    free_list.pop_back();
+    return p;
+  }
+  int32_t free_pages() const { return (int32_t)free_list.size(); }
+};
+
+extern "C" {
+
+int cb_builder_create(const cb_builder_config* config, cb_builder** out) {
+  cb::clear_error();
+  if (!config || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_create: null argument");
+  const cb_builder_config& c = *config;
+  if (c.page_size != CB_PAGE_SIZE)
+    return cb::fail(CB_ERR_UNSUPPORTED, "page_size must be %d (got %d)", CB_PAGE_SIZE, c.page_size);
+  if (c.max_batch_tokens < 1 || c.max_requests_per_batch < 1 || c.num_pages < 1 ||
+      (int64_t)c.num_pages * CB_PAGE_SIZE >= (int64_t(1) << 31))
+    return cb::fail(CB_ERR_INVALID, "budgets and pool size must be positive (pool < 2^27 pages)");
+  if (c.max_prefill_chunk < 0 || !(c.safety_margin >= 0.0f && c.safety_margin < 1.0f))
+    return cb::fail(CB_ERR_INVALID, "max_prefill_chunk must be >= 0 and safety_margin in [0, 1)");
+  cb_builder* b = new (std::nothrow) cb_builder();
+  if (!b) return cb::fail(CB_ERR_INVALID, "out of host memory");
+  b->cfg = c;
+  b->free_list.resize(c.num_pages);
+  for (int32_t i = 0; i < c.num_pages; ++i) b->free_list[i] = c.num_pages - 1 - i;
+  if (c.page_shuffle_seed != 0) {
+    uint64_t st = c.page_shuffle_seed;
+    for (int32_t i = c.num_pages - 1; i > 0; --i) {
+      int32_t j = (int32_t)(splitmix64(st) % (uint64_t)(i + 1));
+      std::swap(b->free_list[i], b->free_list[j]);
+    }
+  }
+  *out = b;
+  return CB_OK;
+}
+
+int cb_builder_clone(const cb_builder* b, cb_builder** out) {
+  cb::clear_error();
+  if (!b || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_clone: null argument");
+  cb_builder* c = new (std::nothrow) cb_builder();
+  if (!c) return cb::fail(CB_ERR_INVALID, "out of host memory");
+  c->cfg = b->cfg;
+  c->free_list = b->free_list;
+  c->arrivals = b->arrivals;
+  c->steps = b->steps;
+  c->total_stalls = b->total_stalls;
+  c->total_finished = b->total_finished;
+  for (const auto& r : b->reqs) {
+    c->reqs.emplace_back(new Request(*r));
+    c->by_id[r->id] = c->reqs.back().get();
+  }
+  *out = c;
+  return CB_OK;
+}
+
+void cb_builder_destroy(cb_builder* b) { delete b; }
+
+int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t output_len,
+                      int32_t tokens_cached) {
+  cb::clear_error();
+  if (!b) return cb::fail(CB_ERR_INVALID, "cb_builder_submit: null builder");
+  if (b->by_id.count(req_id)) return cb::fail(CB_ERR_INVALID, "duplicate request id %lld", (long long)req_id);
+  if (prompt_len < 1 || output_len < 1 || tokens_cached < 0)
+    return cb::fail(CB_ERR_INVALID, "prompt_len and output_len must be >= 1, tokens_cached >= 0");
+  const int64_t final_kv = (int64_t)prompt_len + output_len - 1;
+  if (tokens_cached > 0 && tokens_cached >= final_kv)
+    return cb::fail(CB_ERR_INVALID, "request %lld has nothing left to do", (long long)req_id);
+  if (cb::ceil_div(final_kv, CB_PAGE_SIZE) > b->cfg.num_pages)
+    return cb::fail(CB_ERR_CAPACITY, "request %lld needs %lld pages; the pool has %d", (long long)req_id,
+                    (long long)cb::ceil_div(final_kv, CB_PAGE_SIZE), b->cfg.num_pages);
+  auto r = std::make_unique<Request>();
+  r->id = req_id;
+  r->prompt_len = prompt_len;
+  r->output_len = output_len;
+  r->arrival = b->arrivals;
+  if (tokens_cached > 0) {
+    int32_t need = (int32_t)cb::ceil_div(tokens_cached, CB_PAGE_SIZE);
+    if (need > b->free_pages())
+      return cb::fail(CB_ERR_CAPACITY, "import of %lld needs %d pages; %d free", (long long)req_id, need,
+                      b->free_pages());
+    for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
+    r->cached = tokens_cached;
+    if (tokens_cached < prompt_len) {
+      r->state = State::Prefilling;
+    } else {
+      r->state = State::Decoding;
+      r->generated = tokens_cached - prompt_len + 1;
+    }
+  }
+  b->arrivals++;
+  b->by_id[req_id] = r.get();
+  b->reqs.push_back(std::move(r));
+  return CB_OK;
+}
+
+int cb_builder_step(cb_builder* b, cb_step* out) {
+  cb::clear_error();
+  if (!b || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_step: null argument");
+  const cb_builder_config& c = b->cfg;
+  b->o_req_ids.clear();
+  b->o_finished.clear();
+  b->o_stalled.clear();
+
+  // 0. release what finished in the previous step (arrival order)
+  {
+    std::vector<std::unique_ptr<Request>> keep;
+    keep.reserve(b->reqs.size());
+    for (auto& r : b->reqs) {
+      if (r->state == State::Finished) {
+        for (int32_t p : r->pages) b->free_list.push_back(p);
+        b->o_finished.push_back(r->id);
+        b->by_id.erase(r->id);
+        b->total_finished++;
+      } else {
+        keep.push_back(std::move(r));
+      }
+    }
+    b->reqs.swap(keep);
+  }
+
+  struct Pick { Request* r; int32_t n; bool decode; };
+  std::vector<Pick> picks;
+  int32_t tokens_left = c.max_batch_tokens;
+  int32_t slots_left = c.max_requests_per_batch;
+  int32_t new_pages = 0;
+
+  // 1. active decodes, one token each
+  for (auto& up : b->reqs) {
+    Request* r = up.get();
+    if (r->state != State::Decoding) continue;
+    if (tokens_left < 1 || slots_left < 1) break;
+    int32_t need = (r->cached % CB_PAGE_SIZE == 0) ? 1 : 0;
+    if (need > b->free_pages()) { b->o_stalled.push_back(r->id); continue; }
+    if (need) { r->pages.push_back(b->take_page()); new_pages++; }
+    picks.push_back({r, 1, true});
+    tokens_left -= 1;
+    slots_left -= 1;
+  }
+  // 2. active prefills, as many tokens as possible
+  for (auto& up : b->reqs) {
+    Request* r = up.get();
+    if (r->state != State::Prefilling) continue;
+    if (tokens_left < 1 || slots_left < 1) break;
+    int64_t chunk = std::min<int64_t>(r->prompt_len - r->cached, tokens_left);
+    if (c.max_prefill_chunk > 0) chunk = std::min<int64_t>(chunk, c.max_prefill_chunk);
+    chunk = std::min<int64_t>(chunk, ((int64_t)r->pages.size() + b->free_pages()) * CB_PAGE_SIZE - r->cached);
+    if (chunk <= 0) { b->o_stalled.push_back(r->id); continue; }
+    int32_t need = (int32_t)(cb::ceil_div(r->cached + chunk, CB_PAGE_SIZE) - (int64_t)r->pages.size());
+    for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
+    new_pages += need;
+    picks.push_back({r, (int32_t)chunk, false});
+    tokens_left -= (int32_t)chunk;
+    slots_left -= 1;
+  }
+  // 3. waiting requests, arrival order, strict head of line
+  for (auto& up : b->reqs) {
+    Request* r = up.get();
+    if (r->state != State::Waiting) continue;
+    if (tokens_left < 1 || slots_left < 1) break;
+    int32_t chunk = std::min(r->prompt_len, tokens_left);
+    if (c.max_prefill_chunk > 0) chunk = std::min(chunk, c.max_prefill_chunk);
+    int32_t need = (int32_t)cb::ceil_div(chunk, CB_PAGE_SIZE);
+    if (need > b->free_pages()) break;
+    if (c.safety_margin > 0.0f &&
+        (double)(b->free_pages() - need) < (double)c.safety_margin * (double)c.num_pages)
+      break;
+    for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
+    new_pages += need;
+    r->state = State::Prefilling;
+    picks.push_back({r, chunk, false});
+    tokens_left -= chunk;
+    slots_left -= 1;
+  }
+
+  // emit the descriptor
+  const int32_t n = (int32_t)picks.size();
+  int32_t stride = 1, num_decodes = 0, max_q = 0, max_ctx = 0;
+  int64_t total = 0;
+  for (const Pick& p : picks) {
+    stride = std::max<int32_t>(stride, (int32_t)p.r->pages.size());
+    num_decodes += p.decode ? 1 : 0;
+    max_q = std::max(max_q, p.n);
+    max_ctx = std::max(max_ctx, p.r->cached + p.n);
+    total += p.n;
+  }
+  b->o_qsl.assign(n + 1, 0);
+  b->o_ctx.assign(n, 0);
+  b->o_off.assign(n, 0);
+  b->o_bt.assign((size_t)n * stride, 0);
+  b->o_slots.assign((size_t)total, 0);
+  int32_t t = 0;
+  for (int32_t s = 0; s < n; ++s) {
+    Request* r = picks[s].r;
+    const int32_t q_len = picks[s].n;
+    b->o_req_ids.push_back(r->id);
+    b->o_qsl[s] = t;
+    b->o_off[s] = r->cached;
+    b->o_ctx[s] = r->cached + q_len;
+    std::copy(r->pages.begin(), r->pages.end(), b->o_bt.begin() + (size_t)s * stride);
+    for (int32_t i = 0; i < q_len; ++i) {
+      const int32_t pos = r->cached + i;
+      b->o_slots[t + i] = r->pages[pos / CB_PAGE_SIZE] * CB_PAGE_SIZE + pos % CB_PAGE_SIZE;
+    }
+    t += q_len;
+    // advance the request's lifecycle
+    r->cached += q_len;
+    if (picks[s].decode) r->generated += 1;
+    else if (r->cached == r->prompt_len) r->generated = 1;
+    if (r->generated >= 1)
+      r->state = (r->generated >= r->output_len) ? State::Finished : State::Decoding;
+  }
+  b->o_qsl[n] = t;
+  b->steps++;
+  b->total_stalls += (int64_t)b->o_stalled.size();
+
+  out->num_seqs = n;
+  out->num_decodes = num_decodes;
+  out->num_tokens = t;
+  out->max_query_len = max_q;
+  out->max_context_len = max_ctx;
+  out->block_table_stride = stride;
+  out->num_finished = (int32_t)b->o_finished.size();
+  out->num_stalled = (int32_t)b->o_stalled.size();
+  out->new_pages = new_pages;
+  out->req_ids = b->o_req_ids.data();
+  out->query_start_loc = b->o_qsl.data();
+  out->context_lens = b->o_ctx.data();
+  out->q_offsets = b->o_off.data();
+  out->block_tables = b->o_bt.data();
+  out->slot_mapping = b->o_slots.data();
+  out->finished_ids = b->o_finished.data();
+  out->stalled_ids = b->o_stalled.data();
+  return CB_OK;
+}
+
+int cb_builder_block_table(const cb_builder* b, int64_t req_id, int32_t* out, int32_t cap, int32_t* n) {
+  cb::clear_error();
+  if (!b || !n || (cap > 0 && !out)) return cb::fail(CB_ERR_INVALID, "cb_builder_block_table: null argument");
+  auto it = b->by_id.find(req_id);
+  if (it == b->by_id.end()) return cb::fail(CB_ERR_INVALID, "unknown request id %lld", (long long)req_id);
+  const auto& pages = it->second->pages;
+  *n = (int32_t)pages.size();
+  const int32_t m = std::min<int32_t>(cap, (int32_t)pages.size());
+  for (int32_t i = 0; i < m; ++i) out[i] = pages[i];
+  return CB_OK;
+}
+
+int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out) {
+  cb::clear_error();
+  if (!b || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_stats_get: null argument");
+  std::memset(out, 0, sizeof(*out));
+  out->num_pages = b->cfg.num_pages;
+  out->free_pages = b->free_pages();
+  for (const auto& r : b->reqs) {
+    switch (r->state) {
+      case State::Waiting: out->num_waiting++; break;
+      case State::Prefilling: out->num_prefilling++; break;
+      case State::Decoding: out->num_decoding++; break;
+      case State::Finished: out->num_finished_pending++; break;
+    }
+    out->used_slots += r->cached;
+  }
+  out->allocated_slots = (int64_t)(b->cfg.num_pages - b->free_pages()) * CB_PAGE_SIZE;
+  out->steps = b->steps;
+  out->total_stalls = b->total_stalls;
+  out->total_finished = b->total_finished;
+  out->fragmentation = out->allocated_slots > 0
+      ? (double)(out->allocated_slots - out->used_slots) / (double)out->allocated_slots : 0.0;
+  return CB_OK;
+}
+
+}  // extern "C"

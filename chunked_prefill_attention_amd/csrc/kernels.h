@@ -1,0 +1,53 @@
+// Host-side interface of the device code: launch helpers and the layout of
+// the attention workspace.  Everything here runs on the host; the kernels
+// live in the .hip files.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace cb {
+
+// Events recorded around the main attention kernel (cb_profile_events);
+// null when profiling is off.  Per host thread.
+extern thread_local hipEvent_t g_prof_start;
+extern thread_local hipEvent_t g_prof_stop;
+
+// Arguments of one attention step, already validated on the host.
+struct AttnArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* qsl;
+  const int32_t* ctx_lens;
+  const int32_t* q_offsets;
+  int32_t num_seqs, num_decodes, num_tokens, max_context_len;
+  int32_t hq, hkv, head_dim, num_pages;
+  float scale;
+  void* out;
+  void* workspace;
+};
+
+// Sizing of the bf16 path's workspace; a pure function of host scalars so
+// that cb_attention_workspace_bytes and cb_attention_step agree.
+struct Bf16Plan {
+  int32_t split_pages;   // pages per decode wave (split-K unit)
+  int64_t dec_cap;       // bound on (sequence, split) decode items
+  int64_t pf_cap;        // bound on (sequence, 128-row tile) prefill items
+  size_t off_counts, off_dec_first, off_dec_items, off_pf_items, off_part_ml, off_part_o;
+  size_t bytes;
+};
+Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
+                   int32_t hkv, int32_t head_dim, int32_t max_context_len);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t head_dim,
+                            int32_t num_pages, int32_t elem_bytes, hipStream_t stream);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention_bf16(const AttnArgs& a, const Bf16Plan& plan, hipStream_t stream);
+
+}  // namespace cb

@@ -1,0 +1,300 @@
+/*
+ * cb.h -- C ABI of the chunked-prefill + decode paged-attention step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One engine step of a continuous-batching server runs, for one attention
+ * layer:
+ *   1. cb_builder_step     host: choose this step's requests and tokens,
+ *                          allocate KV pages, emit the ragged step descriptor;
+ *   2. cb_kv_append        device: write this step's K/V rows into the pages
+ *                          through the slot mapping;
+ *   3. cb_attention_step   device: one ragged launch in which every query row
+ *                          (decode tokens and prefill-chunk tokens alike)
+ *                          attends causally to its own sequence's KV history.
+ *
+ * Sources of the semantics (the web pages this library is built from):
+ *   [GLOSS]  Ultralytics glossary, "Chunked Prefill": section "How chunked
+ *            prefill works" -- each chunk attends, under a causal mask over
+ *            absolute positions, to the cached K/V of all earlier chunks plus
+ *            itself; the result equals one-shot prefill.  Also the scheduling
+ *            rule: one token per running decode, then chunks of waiting
+ *            prompts fill the remaining token budget.
+ *   [CBA]    Hugging Face transformers, "Continuous batching architecture":
+ *            sections "Request lifecycle", "Chunked prefill", "Scheduler",
+ *            "FIFO", "Memory management", "Admission".
+ *   [VLLM]   AI Engineering from Scratch, "vLLM serving internals": sections
+ *            "PagedAttention as virtual memory" (16-token blocks, per-sequence
+ *            block tables) and "What the scheduler looks like".
+ *
+ * Conventions for every call:
+ *   - No call allocates device memory, synchronises the device or blocks on
+ *     the stream; device work is enqueued on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream) on the caller's current device.
+ *   - Pointers named "device" must be device memory owned by the caller and
+ *     stay valid until the enqueued work completes.  Pointers named "host"
+ *     are read before the call returns.
+ *   - Every call returns a status (CB_OK or a negative CB_ERR_*).  On error,
+ *     nothing has been enqueued (except CB_ERR_DEVICE, which reports a failed
+ *     launch) and cb_last_error() holds a thread-local message.
+ *   - Page size is fixed at 16 tokens ([VLLM] "PagedAttention as virtual
+ *     memory": default block of 16 tokens).
+ *
+ * KV cache layout (one attention layer; pages are the physical blocks):
+ *   k_cache[num_pages][Hkv][16][D]   token-major within a (page, head) slab
+ *   v_cache[num_pages][Hkv][D][16]   token-minor within a (page, head) slab
+ *   slot = page * 16 + offset; logical position p of sequence s lives in slot
+ *   block_tables[s * stride + p / 16] * 16 + p % 16.
+ * Element type: float32 (CB_F32) or bfloat16 bits (CB_BF16), same for q, k,
+ * v and out.
+ */
+#ifndef CB_H
+#define CB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------------------------
+ * Status and types
+ * ------------------------------------------------------------------------- */
+enum {
+  CB_OK = 0,
+  CB_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent shape  */
+  CB_ERR_UNSUPPORTED = -2, /* head_dim, page_size, dtype or group size not built */
+  CB_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required        */
+  CB_ERR_DEVICE = -4,      /* a kernel launch failed (hipGetLastError)          */
+  CB_ERR_CAPACITY = -5     /* a request can never fit the page pool             */
+};
+
+enum { CB_F32 = 0, CB_BF16 = 1 };
+
+#define CB_PAGE_SIZE 16
+
+/* Short static name of a status code ("CB_OK", "CB_ERR_INVALID", ...). */
+const char* cb_status_string(int status);
+
+/* Detail of the last error on the calling thread; "" if none.  Valid until the
+ * thread's next cb_* call. */
+const char* cb_last_error(void);
+
+/* ABI version of this header (increments on incompatible change). */
+int cb_abi_version(void);
+
+/* ----------------------------------------------------------------------------
+ * cb_kv_append -- write this step's new K/V rows into their cache slots.
+ *
+ * [GLOSS] "How chunked prefill works": a chunk's own keys and values are
+ * cached before it attends, and later chunks read them from the cache.
+ * [VLLM] "PagedAttention as virtual memory": slots live in fixed 16-token
+ * blocks mapped through the sequence's block table.
+ *
+ *   k_new, v_new   device, [num_tokens][num_kv_heads][head_dim], contiguous
+ *   k_cache        device, [num_pages][num_kv_heads][16][head_dim]
+ *   v_cache        device, [num_pages][num_kv_heads][head_dim][16]
+ *   slot_mapping   device int32 [num_tokens]; token t goes to slot
+ *                  slot_mapping[t]; a negative slot writes nothing (padding).
+ *   dtype          CB_F32 or CB_BF16; rows are copied bit for bit.
+ *
+ * Preconditions on device data (not checked on the host, which never reads
+ * device memory): no two tokens name one slot.  A slot >= num_pages * 16 is
+ * skipped by the kernel rather than written out of bounds.
+ * Errors: CB_ERR_INVALID (null pointer with num_tokens > 0, negative sizes,
+ * num_pages * 16 >= 2^31), CB_ERR_UNSUPPORTED (page_size != 16, head_dim not
+ * 64 or 128, unknown dtype), CB_ERR_DEVICE.  num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+int cb_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                 const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t num_pages, int32_t page_size, int32_t dtype,
+                 void* stream);
+
+/* ----------------------------------------------------------------------------
+ * cb_attention_workspace_bytes -- device scratch that cb_attention_step needs.
+ *
+ * Host-only arithmetic on the same scalars cb_attention_step receives; an
+ * upper bound for the step's work lists and split-K partial results.  Returns
+ * 0 when no workspace is needed, and (size_t)-1 for invalid arguments.
+ * ------------------------------------------------------------------------- */
+size_t cb_attention_workspace_bytes(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t dtype);
+
+/* ----------------------------------------------------------------------------
+ * cb_attention_step -- causal attention of every query row of the step.
+ *
+ * [GLOSS] "How chunked prefill works": query row i of sequence s sits at
+ * absolute position p = q_offsets[s] + i and attends to logical KV positions
+ * 0..p (inclusive) of the same sequence; with
+ *   x_j = scale * <q_row, k_j>,  w_j = exp(x_j - max x),  out = sum w_j v_j / sum w_j.
+ * Decode requests are one-token chunks ([CBA] "Request lifecycle").
+ *
+ *   q, out            device, [num_tokens][num_q_heads][head_dim]
+ *   k_cache, v_cache  device, layouts in the header comment; they must already
+ *                     hold this step's tokens (cb_kv_append on the same
+ *                     stream first)
+ *   block_tables      device int32 [num_seqs][block_table_stride]; entries
+ *                     past ceil(context_lens[s]/16) are never read
+ *   query_start_loc   device int32 [num_seqs + 1]; sequence s owns query rows
+ *                     query_start_loc[s] .. query_start_loc[s+1]-1; [0] = 0
+ *                     and [num_seqs] = num_tokens
+ *   context_lens      device int32 [num_seqs]; KV length including this step
+ *   q_offsets         device int32 [num_seqs]; = context_lens - q_len
+ *   num_decodes       the first num_decodes sequences have q_len == 1 and take
+ *                     the split-K decode path; the rest take the prefill-tile
+ *                     path (any q_len >= 0, including 1)
+ *   max_context_len   host upper bound of context_lens (sizes the grid)
+ *   Grouped-query mapping: query head h reads KV head h / (Hq / Hkv).
+ *   scale             softmax scale (1/sqrt(head_dim) by convention)
+ *   workspace         device, >= cb_attention_workspace_bytes(...) bytes
+ *                     (may be NULL when that is 0); contents on entry do not
+ *                     matter; two calls that share a workspace must be
+ *                     ordered on one stream
+ *
+ * Values in cache slots at or past context_lens[s] (or NaN there) do not
+ * affect the output.  Page ids >= num_pages are read as zero pages instead of
+ * faulting.  Device-side preconditions that are not checked: the
+ * query_start_loc / context_lens / q_offsets relations above and
+ * context_lens <= max_context_len.
+ * Errors: CB_ERR_INVALID (null pointers, negative or inconsistent sizes,
+ * Hq % Hkv != 0, stride < ceil(max_context_len/16)), CB_ERR_UNSUPPORTED
+ * (page_size != 16, head_dim not 64/128, group size Hq/Hkv > 16, dtype),
+ * CB_ERR_WORKSPACE, CB_ERR_DEVICE.  num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+int cb_attention_step(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t block_table_stride,
+                      const int32_t* query_start_loc, const int32_t* context_lens,
+                      const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes,
+                      int32_t num_tokens, int32_t max_context_len, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t num_pages, float scale, int32_t dtype, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * cb_profile_events -- timing hook for the main attention kernel.
+ *
+ * Not on the pages; a measurement aid.  start_event / stop_event are
+ * hipEvent_t handles (passed as void*) that the caller created with timing
+ * enabled.  Subsequent cb_attention_step calls made by the calling thread
+ * record start_event on their stream right before the main ragged attention
+ * kernel and stop_event right after it, so hipEventElapsedTime gives that
+ * kernel's duration alone (plan and combine kernels excluded).  Passing NULL,
+ * NULL turns the hook off.  Host bookkeeping only; returns CB_OK, or
+ * CB_ERR_INVALID when exactly one handle is NULL.
+ * ------------------------------------------------------------------------- */
+int cb_profile_events(void* start_event, void* stop_event);
+
+/* ----------------------------------------------------------------------------
+ * FIFO batch builder (host only; touches no device).
+ *
+ * [CBA] "Scheduler": three limits per forward pass -- the token budget
+ * (max_batch_tokens), the cache budget (KV pages) and the request cap
+ * (max_requests_per_batch).  [CBA] "FIFO": active decodes first, then active
+ * prefills, then waiting requests in arrival order.  [CBA] "Chunked
+ * prefill": a prompt beyond the remaining budget is processed for as many
+ * tokens as possible and resumes next step.  [CBA] "Admission": a request that
+ * cannot be held is not admitted and nothing is allocated; below
+ * safety_margin of free pages new prefills wait while active work continues.
+ * [VLLM] "What the scheduler looks like": finished requests release their
+ * blocks at the top of the step; the head of the waiting queue is admitted
+ * while it fits (strict head of line).
+ *
+ * Chunk length = min(remaining prompt, remaining token budget,
+ * max_prefill_chunk if > 0).  An active prefill is cut further to what its
+ * held plus free pages can hold (stalled if that is 0).  A decode whose cached
+ * length is a multiple of 16 needs one new page; with none free it is stalled
+ * (skipped this step).  A waiting request is admitted only if its first
+ * chunk's pages are free and free - needed >= safety_margin * num_pages.
+ * The prefill step that completes a prompt yields output token 1; each decode
+ * step yields one more; a request finishing in a step is released (pages
+ * freed, id reported) at the start of the next step.
+ * ------------------------------------------------------------------------- */
+typedef struct cb_builder cb_builder;
+
+typedef struct {
+  int32_t max_batch_tokens;       /* >= 1 */
+  int32_t max_requests_per_batch; /* >= 1 */
+  int32_t num_pages;              /* pool size, >= 1, num_pages * 16 < 2^31 */
+  int32_t page_size;              /* must be 16 */
+  int32_t max_prefill_chunk;      /* 0 = no cap */
+  float safety_margin;            /* in [0, 1); 0 disables the margin */
+  uint64_t page_shuffle_seed;     /* 0: pages handed out 0, 1, 2, ...; else the
+                                     initial free list is a seeded permutation */
+} cb_builder_config;
+
+/* The step descriptor.  Arrays are owned by the builder and stay valid until
+ * the next cb_builder_step / cb_builder_destroy on the same builder. */
+typedef struct {
+  int32_t num_seqs;           /* scheduled sequences; decodes come first */
+  int32_t num_decodes;
+  int32_t num_tokens;         /* sum of q_len */
+  int32_t max_query_len;
+  int32_t max_context_len;
+  int32_t block_table_stride; /* max pages held by a scheduled sequence (>= 1) */
+  int32_t num_finished;       /* released at the start of this step */
+  int32_t num_stalled;
+  int32_t new_pages;          /* pages allocated this step */
+  const int64_t* req_ids;         /* [num_seqs] */
+  const int32_t* query_start_loc; /* [num_seqs + 1] */
+  const int32_t* context_lens;    /* [num_seqs] */
+  const int32_t* q_offsets;       /* [num_seqs] */
+  const int32_t* block_tables;    /* [num_seqs * block_table_stride], unused = 0 */
+  const int32_t* slot_mapping;    /* [num_tokens] */
+  const int64_t* finished_ids;    /* [num_finished] */
+  const int64_t* stalled_ids;     /* [num_stalled] */
+} cb_step;
+
+typedef struct {
+  int32_t num_pages;
+  int32_t free_pages;
+  int32_t num_waiting;
+  int32_t num_prefilling;
+  int32_t num_decoding;
+  int32_t num_finished_pending; /* finished, pages released next step */
+  int64_t used_slots;           /* sum of cached tokens of live requests */
+  int64_t allocated_slots;      /* pages in use * 16 */
+  int64_t steps;
+  int64_t total_stalls;
+  int64_t total_finished;
+  double fragmentation;         /* (allocated - used) / allocated; 0 if none */
+} cb_builder_stats;
+
+/* Create a builder.  Errors: CB_ERR_INVALID (null, bad budget or margin),
+ * CB_ERR_UNSUPPORTED (page_size != 16). */
+int cb_builder_create(const cb_builder_config* config, cb_builder** out);
+
+/* Deep copy of a builder's whole state (requests, pages, free list). */
+int cb_builder_clone(const cb_builder* b, cb_builder** out);
+
+void cb_builder_destroy(cb_builder* b);
+
+/* Submit a request.  tokens_cached == 0: it waits in arrival order.
+ * tokens_cached > 0 imports an in-flight request whose pages are allocated
+ * now (the caller writes their K/V, slots from cb_builder_block_table): an
+ * active prefill if tokens_cached < prompt_len, else a decode that has
+ * produced tokens_cached - prompt_len + 1 output tokens.
+ * Errors: CB_ERR_INVALID (duplicate id, prompt_len < 1, output_len < 1,
+ * tokens_cached < 0, nothing left to do), CB_ERR_CAPACITY
+ * (ceil((prompt_len + output_len - 1) / 16) > num_pages, or an import whose
+ * pages are not free). */
+int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t output_len,
+                      int32_t tokens_cached);
+
+/* Run the scheduler for one engine step and fill *out.  A step with nothing
+ * schedulable returns CB_OK with num_seqs == 0. */
+int cb_builder_step(cb_builder* b, cb_step* out);
+
+/* Copy request req_id's block table (physical page ids in logical order) into
+ * out[0 .. cap-1]; *n receives the number of pages it holds.
+ * Errors: CB_ERR_INVALID (unknown id, null pointers). */
+int cb_builder_block_table(const cb_builder* b, int64_t req_id, int32_t* out, int32_t cap,
+                           int32_t* n);
+
+int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CB_H */

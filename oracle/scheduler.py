@@ -54,6 +54,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import numpy as np
+
 WAITING, PREFILLING, DECODING, FINISHED = "waiting", "prefilling", "decoding", "finished"
 
 
@@ -117,7 +119,8 @@ class FifoScheduler:
         self.num_pages = num_pages
         self.page = page_size
         self.chunk_cap = max_prefill_chunk
-        self.margin = float(safety_margin)
+        # the margin is a float32 configuration value; compare in float64
+        self.margin = float(np.float32(safety_margin))
         self.free = num_pages
         self.requests: dict[int, Request] = {}
         self._arrivals = 0

@@ -1,0 +1,146 @@
+"""The C++ FIFO builder against the plain-Python scheduler oracle (CPU only).
+
+The schedule (which requests, how many tokens, at which offsets, in which
+order, what finishes and what stalls) is unique under the documented
+readings, so it must agree exactly.  Physical page ids are not unique; they
+are checked for consistency: the slot mapping equals the block-table
+arithmetic, a request's table never changes once written, and no page is
+held by two live requests.
+"""
+import numpy as np
+import pytest
+
+import chunked_prefill_attention_amd as cb
+from oracle.scheduler import FifoScheduler, SchedulerError
+from oracle import paging
+import workloads as wl
+
+
+def _pair(**kw):
+    o = FifoScheduler(kw["max_batch_tokens"], kw["max_requests"], kw["num_pages"],
+                      max_prefill_chunk=kw.get("chunk", 0), safety_margin=kw.get("margin", 0.0))
+    b = cb.Builder(kw["max_batch_tokens"], kw["max_requests"], kw["num_pages"],
+                   max_prefill_chunk=kw.get("chunk", 0), safety_margin=kw.get("margin", 0.0),
+                   page_shuffle_seed=kw.get("shuffle", 0))
+    return o, b
+
+
+def _compare_step(so, sb, tables):
+    assert [x.req_id for x in so.seqs] == sb.req_ids.tolist()
+    assert so.num_decodes == sb.num_decodes
+    assert so.num_tokens == sb.num_tokens
+    assert [x.q_len for x in so.seqs] == sb.q_lens.tolist()
+    assert [x.q_offset for x in so.seqs] == sb.q_offsets.tolist()
+    assert [x.context_len for x in so.seqs] == sb.context_lens.tolist()
+    assert sorted(so.finished) == sorted(sb.finished_ids.tolist())
+    assert so.stalled == sb.stalled_ids.tolist()
+    assert so.new_pages == sb.new_pages
+    held = {}
+    for s, x in enumerate(so.seqs):
+        row = sb.block_tables[s, :x.pages]
+        assert (sb.block_tables[s, x.pages:] == 0).all()
+        prev = tables.get(x.req_id)
+        if prev is not None:
+            assert np.array_equal(row[:len(prev)], prev)          # tables only grow
+        tables[x.req_id] = row.copy()
+        a, e = sb.query_start_loc[s], sb.query_start_loc[s + 1]
+        assert np.array_equal(sb.slot_mapping[a:e], paging.slots_for(row, x.q_offset, x.context_len))
+        for pg in row.tolist():
+            assert pg not in held, "page shared by two requests"
+            held[pg] = x.req_id
+    for rid in so.finished:
+        tables.pop(rid, None)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_traces_match_oracle(seed):
+    rng = np.random.default_rng(100 + seed)
+    kw = dict(max_batch_tokens=int(rng.integers(8, 300)), max_requests=int(rng.integers(1, 12)),
+              num_pages=int(rng.integers(20, 120)), chunk=int(rng.choice([0, 0, 16, 33])),
+              margin=float(rng.choice([0.0, 0.15, 0.3])), shuffle=seed)
+    o, b = _pair(**kw)
+    tables = {}
+    nid = 0
+    for step in range(400):
+        for _ in range(int(rng.poisson(0.6))):
+            p, q = int(rng.integers(1, 200)), int(rng.integers(1, 40))
+            cached = int(rng.integers(0, p + q - 1)) if rng.random() < 0.2 else 0
+            err_o = err_b = None
+            try:
+                o.submit(nid, p, q, cached)
+            except SchedulerError as e:
+                err_o = e.kind
+            try:
+                b.submit(nid, p, q, cached)
+            except cb.CbError as e:
+                err_b = {-1: "invalid", -5: "capacity"}[e.status]
+            assert err_o == err_b
+            nid += 1
+        so, sb = o.step(), b.step()
+        _compare_step(so, sb, tables)
+        st = b.stats()
+        assert st["free_pages"] == o.free
+        assert st["used_slots"] == o.used_slots()
+    assert b.stats()["total_stalls"] == o.total_stalls
+
+
+def test_page_example_and_mixed_and_long_prompt_compositions():
+    for w in (wl.page_example(), wl.mixed(), wl.long_prompt()):
+        o, b = _pair(max_batch_tokens=w.max_batch_tokens, max_requests=w.max_requests,
+                     num_pages=w.pool_pages, chunk=w.max_prefill_chunk, margin=w.safety_margin, shuffle=7)
+        for i, (p, q, c) in enumerate(w.requests):
+            o.submit(i, p, q, c)
+            b.submit(i, p, q, c)
+        tables = {}
+        for _ in range(45):
+            _compare_step(o.step(), b.step(), tables)
+
+
+def test_fifo_trace_schedule_matches_oracle():
+    """The 256-request trace (Poisson arrivals, lognormal prompts, geometric outputs)."""
+    reqs = wl.fifo_trace()
+    o, b = _pair(max_batch_tokens=2048, max_requests=128, num_pages=200_000, margin=0.15, shuffle=5)
+    tables = {}
+    pending = list(reqs)
+    step = 0
+    frag = []
+    while pending or not o.idle():
+        while pending and pending[0].arrival_step <= step:
+            r = pending.pop(0)
+            o.submit(r.req_id, r.prompt_len, r.output_len)
+            b.submit(r.req_id, r.prompt_len, r.output_len)
+        _compare_step(o.step(), b.step(), tables)
+        st = b.stats()
+        if st["allocated_slots"]:
+            frag.append(st["fragmentation"])
+        step += 1
+        assert step < 20000
+    assert b.stats()["total_finished"] == len(reqs)
+    assert max(frag) < 0.5 and np.mean(frag) < 0.04    # paged: small internal waste
+
+
+def test_clone_is_independent():
+    b = cb.Builder(64, 8, 100)
+    b.submit(1, 100, 5)
+    c = b.clone()
+    s1, s2 = b.step(), c.step()
+    assert s1.req_ids.tolist() == s2.req_ids.tolist() and s1.num_tokens == s2.num_tokens
+    assert np.array_equal(s1.block_tables, s2.block_tables)
+    b.step()
+    assert b.stats()["steps"] == 2 and c.stats()["steps"] == 1
+
+
+def test_builder_errors():
+    with pytest.raises(cb.CbError) as e:
+        cb.Builder(0, 1, 10)
+    assert e.value.status == -1
+    b = cb.Builder(16, 2, 4)
+    with pytest.raises(cb.CbError) as e:
+        b.submit(1, 100, 1)
+    assert e.value.status == -5
+    b.submit(2, 10, 1)
+    with pytest.raises(cb.CbError) as e:
+        b.submit(2, 10, 1)
+    assert e.value.status == -1
+    with pytest.raises(cb.CbError):
+        b.block_table(99)

@@ -1,0 +1,172 @@
+"""cb_attention_step on the GPU against the fp64 oracle, element by element.
+
+Small and medium steps that span several tiles and ragged tails, every edge
+case of the method (one-token contexts, page-aligned and unaligned ends,
+single-query prefill rows, decodes with many splits, empty sequences,
+grouped-query sizes 1..16), bit-exact indexing probes, and invariances
+(physical page permutation, determinism, NaN in unused slots).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import Step, compare, i32, new_cache, say, to_dev, write_history
+from oracle import attention as ora
+import chunked_prefill_attention_amd as cb
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_all(st: Step, out, what):
+    worst = 0.0
+    for s, (c, n) in enumerate(st.seqs):
+        if n == 0:
+            continue
+        ref = ora.attend(st.q[s], st.k_hist[s], st.v_hist[s], st.scale)
+        am = ora.attend(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale) if st.dtype == "bf16" else None
+        worst = max(worst, compare(st.out_rows(out, s), ref, st.dtype, f"{what} seq {s} (ctx {c}, q {n})", am))
+    return worst
+
+
+CASES = {
+    # name: (seqs [(ctx, q_len)], Hq, Hkv, D)
+    "decode_gqa4": ([(1, 1), (15, 1), (16, 1), (17, 1), (255, 1), (256, 1), (257, 1), (1000, 1), (3000, 1)], 32, 8, 128),
+    "decode_long_splits": ([(9000, 1), (4097, 1), (130, 1)] + [(2000 + 37 * i, 1) for i in range(40)], 16, 2, 128),
+    "prefill_only_gqa4": ([(476 + 1024, 476), (700, 700), (808, 808)], 32, 8, 128),
+    "mixed_small": ([(33, 1), (600, 1), (129, 1), (1500, 476), (70, 70), (1, 1), (300, 17)], 32, 8, 128),
+    "mixed_d64_g1": ([(40, 1), (513, 1), (260, 130), (64, 64), (1000, 5)], 4, 4, 64),
+    "mixed_g2": ([(100, 1), (2100, 1), (777, 250), (31, 31)], 8, 4, 128),
+    "mixed_g8": ([(1100, 1), (5000, 1), (20000 - 19968 + 19968, 32), (1536, 512)], 64, 8, 128),
+    "mixed_g16": ([(800, 1), (77, 1), (300, 45)], 16, 1, 128),
+    "g3_odd": ([(90, 1), (500, 200)], 6, 2, 64),
+    "qlen1_in_prefill_set": ([(500, 1), (20, 1), (1, 1)], 8, 2, 128),
+    "empty_seq_in_prefill_set": ([(300, 1), (50, 0), (200, 60), (10, 0)], 8, 2, 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_matches_oracle(name, dtype):
+    seqs, hq, hkv, d = CASES[name]
+    say(f"step {name} {dtype}")
+    st = Step(seqs, hq, hkv, d, dtype, seed=hash(name) % 1000)
+    if name == "qlen1_in_prefill_set":
+        st.num_decodes = 1            # later q_len == 1 rows go down the prefill path
+    kc, vc = st.upload()
+    out = st.run(kc, vc)
+    worst = _check_all(st, out, name)
+    say(f"  max abs err {worst:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_peaky_scores(dtype):
+    """Large-magnitude queries concentrate the softmax; outputs are O(1)."""
+    st = Step([(700, 1), (2500, 1), (900, 300)], 32, 8, 128, dtype, seed=11, q_std=4.0)
+    kc, vc = st.upload()
+    _check_all(st, st.run(kc, vc), "peaky")
+
+
+def test_page_example_through_builder_f32():
+    """The pages' worked example as four engine steps (fp32, 8 heads x 64, budget 256).
+
+    Each step: builder -> kv_append of the chunk -> attention over the pages.
+    The concatenated outputs must equal one-shot causal attention (the oracle).
+    """
+    w = wl.page_example()
+    q, k, v = wl.page_example_tensors()
+    b = cb.Builder(w.max_batch_tokens, w.max_requests, w.pool_pages + 7, page_shuffle_seed=12345)
+    b.submit(0, 1000, 1)
+    kc, vc = new_cache(w.pool_pages + 7, 8, 64, "f32")   # 7 spare pages stay NaN
+    outs, sizes = [], []
+    while True:
+        s = b.step()
+        if s.num_seqs == 0:
+            break
+        a, e = int(s.q_offsets[0]), int(s.context_lens[0])
+        sizes.append(e - a)
+        cb.kv_append(to_dev(k[a:e], "f32"), to_dev(v[a:e], "f32"), kc, vc, i32(s.slot_mapping))
+        o = cb.attention_step(to_dev(q[a:e], "f32"), kc, vc, i32(s.block_tables), i32(s.query_start_loc),
+                              i32(s.context_lens), i32(s.q_offsets), s.num_decodes, s.max_context_len,
+                              wl.softmax_scale(64))
+        outs.append(o.cpu().numpy())
+    assert sizes == [256, 256, 256, 232]
+    got = np.concatenate(outs)
+    ref = ora.attend(q, k, v, wl.softmax_scale(64))
+    compare(got, ref, "f32", "page example")
+
+
+def test_one_hot_probe_is_bit_exact():
+    """A dominant key at position j makes every row that sees it return V[j] exactly."""
+    d, hkv, hq = 128, 2, 8
+    ctx_list = [1, 16, 17, 100, 255, 4100]
+    for j_frac in (0.0, 0.37, 0.999):
+        seqs = [(c, 1) for c in ctx_list] + [(700, 300)]
+        st = Step(seqs, hq, hkv, d, "bf16", seed=3)
+        for s, (c, n) in enumerate(st.seqs):
+            j = min(int(j_frac * c), c - n)      # visible to every query of the sequence
+            st.k_hist[s][:] = 0.0
+            st.k_hist[s][j, :, 0] = 16.0
+            st.q[s][:] = 0.0
+            st.q[s][:, :, 0] = 128.0              # score gap 2048*scale ~ 181 (log2 units ~ 261)
+        kc, vc = st.upload()
+        out = st.run(kc, vc)
+        for s, (c, n) in enumerate(st.seqs):
+            j = min(int(j_frac * c), c - n)
+            got = st.out_rows(out, s)
+            for h in range(hq):
+                want = np.broadcast_to(st.v_hist[s][j, h // (hq // hkv)], got[:, h].shape)
+                assert np.array_equal(got[:, h], want), (s, c, j, h)
+
+
+def test_physical_permutation_and_determinism_bitwise():
+    st = Step([(3000, 1), (517, 1), (64, 1), (1500, 476), (700, 700)], 32, 8, 128, "bf16", seed=5)
+    kc, vc = st.upload()
+    o1 = st.run(kc, vc).clone()
+    o2 = st.run(kc, vc).clone()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    alt = st.permuted_table(99)
+    kc2, vc2 = st.upload(table=alt)
+    o3 = st.run(kc2, vc2, table=alt)
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_chunk_size_invariance_bf16():
+    """One prompt prefilled in different chunkings matches the oracle each time."""
+    hq, hkv, d, n = 32, 8, 128, 1100
+    k, v = wl.seq_kv(21, 0, 0, n, hkv, d, "bf16")
+    q = wl.seq_q(21, 0, 0, n, hq, d, "bf16")
+    ref = ora.attend(q, k, v, wl.softmax_scale(d))
+    am = ora.attend(q, k, np.abs(v), wl.softmax_scale(d))
+    for chunk in (1100, 512, 256, 100, 17):
+        pages = -(-n // 16) + 5
+        row = wl.permutation(chunk, pages)[: -(-n // 16)].astype(np.int32)
+        kc, vc = new_cache(pages, hkv, d, "bf16")
+        outs = []
+        for a in range(0, n, chunk):
+            e = min(a + chunk, n)
+            write_history(kc, vc, k, v, row, a, e, "bf16")
+            o = cb.attention_step(to_dev(q[a:e], "bf16"), kc, vc, i32(row[None]), i32([0, e - a]), i32([e]),
+                                  i32([a]), 0, e, wl.softmax_scale(d))
+            outs.append(o.float().cpu().numpy())
+        compare(np.concatenate(outs), ref, "bf16", f"chunk {chunk}", am)
+
+
+def test_nan_in_unused_slots_does_not_leak():
+    """Garbage (NaN) in partial-page tails and in unreferenced pages is masked."""
+    st = Step([(17, 1), (33, 1), (4097, 1), (45, 13), (129, 129)], 16, 4, 128, "bf16", seed=8,
+              fill=float("nan"))
+    kc, vc = st.upload()
+    out = st.run(kc, vc)
+    assert torch.isfinite(out.float()).all()
+    _check_all(st, out, "nan tails")
+
+
+def test_bad_page_ids_read_as_zero_pages():
+    """Out-of-range block-table entries must not fault (they read as zeros)."""
+    st = Step([(40, 1), (60, 20)], 8, 2, 128, "bf16", seed=9, fill=0.0)
+    kc, vc = st.upload()
+    bad = st.bt.copy()
+    bad[:, 1] = st.num_pages + 1000
+    out = st.run(kc, vc, table=bad)
+    assert torch.isfinite(out.float()).all()

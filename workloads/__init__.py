@@ -10,7 +10,7 @@ in float32 and rounded to bfloat16 by round-to-nearest-even (through
 ``torch``'s dtype conversion), and returned as float32 arrays holding exactly
 the bf16 values, so the oracle widens exactly what the GPU holds.
 
-K/V of a sequence are generated per 16-token block from a seed made of
+K/V of a sequence are generated per 256-token block from a seed made of
 ``(seed, stream, seq, block)``: any token range of any sequence can be
 regenerated independently, and re-chunking a prompt never changes its
 values.
@@ -22,7 +22,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-BLOCK = 16
+BLOCK = 256   # tokens per independently seeded block of K/V or Q values
 _K, _V, _Q = 1, 2, 3
 
 
@@ -136,7 +136,7 @@ class Workload:
 
 
 def _pages(n: int) -> int:
-    return -(-n // BLOCK)
+    return -(-n // 16)
 
 
 def decode_only(seed: int = 2, n: int = 128, lo: int = 512, hi: int = 4096) -> Workload:
@@ -204,3 +204,23 @@ def fifo_trace(seed: int = 5, n: int = 256, rate: float = 0.5, median_prompt: in
     outputs = rng.geometric(1.0 / mean_output, size=n).astype(np.int64)
     return [TraceRequest(i, int(a), int(p), int(o)) for i, (a, p, o)
             in enumerate(zip(arrive, prompts, outputs))]
+
+
+def step_q(seed: int, step: int, n_tokens: int, n_q_heads: int, head_dim: int, dtype: str) -> np.ndarray:
+    """Query rows of one engine step ``[T, Hq, D]`` (queries are not cached)."""
+    return normal((n_tokens, n_q_heads, head_dim), dtype, seed, 17, step)
+
+
+def device_normal(shape, dtype: str, device, *key: int):
+    """Standard normal values drawn directly in device memory by torch's
+    counter-based generator, seeded from ``key``; bf16 by RNE conversion.
+
+    Used where host generation would dominate a long trace: the oracle side
+    receives a host copy of exactly these values.
+    """
+    import torch
+    seed = int(np.random.SeedSequence([int(k) for k in key]).generate_state(1, dtype=np.uint64)[0]) & ((1 << 63) - 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
