@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcb.so")
+PROBE = os.path.join(PKG, "hbm_probe")   # streaming-bandwidth probe (measurement aid)
 
 ARCH = "gfx950"
 SOURCES = ["cb_api.cpp", "builder.cpp", "kv_append.hip", "attn_f32.hip", "attn_bf16.hip"]
@@ -56,6 +57,11 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc()] + _flags() + [os.path.join(CSRC, "hbm_probe.hip"), "-o", PROBE + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE + ".tmp", PROBE)
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -11,21 +11,24 @@
 // one grid:
 //
 //  * decode item = one wavefront on (sequence, KV head, split of the page
-//    list).  It streams its pages straight from HBM into registers (one
-//    16-token page of K and of V per iteration, the next page's loads in
-//    flight), scores the G query heads that share the KV head with one
-//    16x16x32 bf16 MFMA per 32 dims (keys as rows, heads as columns), keeps
-//    an online softmax per head, and accumulates P V with 16x16x16 bf16
-//    MFMAs.  Partial (max, sum, O) go to the workspace when the sequence has
-//    more than one split; a combine kernel merges them by log-sum-exp.
+//    list).  It streams its pages straight from HBM into registers (a ring of
+//    page buffers keeps the next pages' loads in flight), scores the G query
+//    heads that share the KV head with one 16x16x32 bf16 MFMA per 32 dims
+//    (keys as rows, heads as columns), keeps an online softmax per head, and
+//    accumulates P V with 16x16x16 bf16 MFMAs.
 //  * prefill item = one 256-thread workgroup on (sequence, KV head, tile of
-//    128 query rows), where a row is a (query token, query head of the
-//    group) pair so the G heads sharing a KV head read K/V once.  Per
-//    64-key tile the workgroup stages K and V pages in LDS; each wavefront
-//    computes S^T = K Q^T for its 32 rows with 32x32x16 bf16 MFMAs, applies
-//    the causal mask only on tiles that straddle its diagonal, updates the
-//    online softmax and accumulates O^T = V^T P^T.  Tiles wholly above the
-//    diagonal are never loaded.
+//    128 query rows, range of keys), where a row is a (query token, query
+//    head of the group) pair so the G heads sharing a KV head read K/V once.
+//    Per 64-key tile the workgroup stages K and V pages in LDS (double
+//    buffered: the next tile's global loads are in flight while the current
+//    tile is computed); each wavefront computes S^T = K Q^T for its 32 rows
+//    with 32x32x16 bf16 MFMAs, masks only the tiles that straddle its
+//    diagonal, updates the online softmax and accumulates O^T = V^T P^T.
+//    Tiles wholly above the diagonal are never loaded.  Long key ranges are
+//    cut into several items so that a long chunk spreads over every CU.
+//
+// Items with more than one split write unnormalised partial results (row
+// max, row sum, O); the combine kernel merges them by log-sum-exp.
 //
 // Layouts: K pages are token-major ([16][D] per (page, head)), so a lane's
 // MFMA A-operand (one key, 8 consecutive dims) is one 16-byte load.  V pages
@@ -33,11 +36,15 @@
 // 8 consecutive keys) is one or two 8-byte loads, and the B-operand P^T comes
 // straight from the score accumulator registers without any shuffle.
 //
-// Numerics: bf16 inputs, fp32 MFMA accumulation, softmax in fp32 on the
-// base-2 scale (scores multiplied by scale*log2(e)), probabilities rounded to
-// bf16 for the P V product, output rounded to bf16 (round to nearest even).
-// Cache slots at or past the context length are masked by select and their V
-// entries zeroed, so garbage or NaN there never reaches the output.
+// Numerics: bf16 inputs, fp32 MFMA accumulation, softmax in fp32 (scores kept
+// in raw units; exponentials are exp2(s*scale*log2(e) - m*scale*log2(e)) with
+// one FMA), probabilities rounded to bf16 for the P V product, output
+// rounded to bf16 (round to nearest even).  The running max is raised only
+// when a score exceeds it by more than 2^3 in exponent units, so the
+// accumulator rescale is usually skipped; weights stay <= 2^8, exact in the
+// normalisation.  Cache slots at or past the context length are masked by
+// select and their V entries zeroed, so garbage or NaN there never reaches
+// the output.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -52,6 +59,22 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// Tunables (compile-time).  Pages of K/V each decode wavefront keeps in
+// flight ahead of the page it is computing on, and its occupancy target.
+#ifndef CB_DEC_PREFETCH
+#define CB_DEC_PREFETCH 2
+#endif
+#ifndef CB_DEC_WAVES_PER_SIMD
+#define CB_DEC_WAVES_PER_SIMD 2
+#endif
+#ifndef CB_NONTEMPORAL_KV
+#define CB_NONTEMPORAL_KV 0
+#endif
+// exponent headroom before the running max is raised (log2 units)
+#ifndef CB_RESCALE_SLACK
+#define CB_RESCALE_SLACK 8.0f
+#endif
+
 constexpr int PF_ROWS = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int PF_KEYS = 64;   // keys per prefill tile (4 pages)
 constexpr float LOG2E = 1.4426950408889634f;
@@ -65,20 +88,24 @@ struct Params {
   const int32_t* ctx_lens;
   const int32_t* q_off;
   uint16_t* out;
-  int32_t* counts;      // [0] decode items, [1] prefill items
-  int32_t* dec_first;   // [num_decodes] first decode item of each sequence
-  int2* dec_items;      // (sequence, split)
-  int2* pf_items;       // (sequence, row tile)
-  float2* part_ml;      // [decode wave][G] (running max in log2 units, sum)
-  float* part_o;        // [decode wave][G][D] unnormalised
+  int4* dec_items;       // (sequence, split, context length, query row); sequence -1 = no work
+  int4* pf_items;        // (sequence, row tile, key split, number of splits); -1 = no work
+  int4* pf_tiles;        // (sequence, row tile, first item, number of splits); -1 = none
+  int32_t* dec_first;    // [num_decodes] first decode item of each sequence
+  float2* dec_ml;        // [decode wave][G] (running max in raw score units, sum)
+  float* dec_o;          // [decode wave][G][D] unnormalised
+  float2* pf_ml;         // [prefill item][PF_ROWS]
+  float* pf_o;           // [prefill item][PF_ROWS][D]
   int32_t bt_stride;
   int32_t num_seqs, num_decodes;
   int32_t hq, hkv, G;
   int32_t num_pages;
-  int32_t split_pages;
-  int32_t pf_blocks;    // grid blocks reserved for prefill items
-  int32_t dec_cap, pf_cap;
-  float scale_log2;     // softmax scale * log2(e)
+  int32_t split_pages;   // pages per decode item
+  int32_t pf_split_keys; // keys per prefill item (multiple of PF_KEYS)
+  int32_t pf_blocks;     // grid blocks reserved for prefill items
+  int32_t dec_cap, pf_tile_cap, pf_item_cap;
+  int32_t comb_dec_blocks;
+  float scale_log2;      // softmax scale * log2(e)
 };
 
 template <int D>
@@ -87,7 +114,8 @@ struct PfLds {
   static constexpr int VROW = 40;          // padded (page, dim) row of 16 tokens (bytes)
   static constexpr int K_BYTES = PF_KEYS * KROW;
   static constexpr int V_BYTES = (PF_KEYS / 16) * D * VROW;
-  static constexpr int BYTES = K_BYTES + V_BYTES;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int BYTES = 2 * STAGE;  // double buffered
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -105,63 +133,121 @@ __device__ __forceinline__ uint32_t keep16(uint32_t w, int first_elem, int n) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// -m*c for the exponent FMA; 0 while no key has been seen (m = -inf), so that
+// masked scores (-inf) still give exp2(-inf) = 0 instead of NaN.
+__device__ __forceinline__ float neg_scaled(float m, float c) { return m == -INFINITY ? 0.f : -m * c; }
+
+// Streaming loads of K/V pages: each byte is used once per launch.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+#if CB_NONTEMPORAL_KV
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ uint2 stream_load(const uint2* p) {
+#if CB_NONTEMPORAL_KV
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+#else
+  return *p;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Plan: one workgroup turns the per-sequence lengths (device data) into
 // compact work lists, so the main grid needs only host-side upper bounds.
+// Unused list slots get sequence -1.
 // ---------------------------------------------------------------------------
-__device__ int block_exclusive_scan(int v, int* sh, int& total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int add = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
   }
-  total = sh[1023];
-  const int incl = sh[tid];
+  return v;
+}
+
+// Exclusive scan over the 1024 threads of the block; `total` gets the sum.
+__device__ int block_exclusive_scan(int v, int* sh, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int incl = wave_inclusive_scan(v);
+  if (lane == 63) sh[wv] = incl;
   __syncthreads();
-  return incl - v;
+  if (wv == 0) {
+    const int x = lane < 16 ? sh[lane] : 0;
+    const int xi = wave_inclusive_scan(x);
+    if (lane < 16) sh[16 + lane] = xi - x;  // exclusive prefix of each wave's total
+    if (lane == 15) sh[32] = xi;
+  }
+  __syncthreads();
+  total = sh[32];
+  const int r = sh[16 + wv] + incl - v;
+  __syncthreads();  // sh is reused by the next call
+  return r;
+}
+
+// keys a prefill row tile needs: up to the last row's position (and the context)
+__device__ __forceinline__ int tile_key_end(int tile, int L, int G, int ctx, int off) {
+  const int last_row = min(tile * PF_ROWS + PF_ROWS, L * G) - 1;
+  return min(ctx, off + last_row / G + 1);
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
-  __shared__ int sh[1024];
+  __shared__ int sh[40];
   const int tid = threadIdx.x;
+  // decode items: (sequence, split) for every split of every decode sequence
   int carry = 0;
   for (int base = 0; base < p.num_decodes; base += 1024) {
     const int s = base + tid;
-    int n = 0;
+    int n = 0, ctx = 0, t = 0;
     if (s < p.num_decodes) {
-      const int ctx = p.ctx_lens[s];
+      ctx = p.ctx_lens[s];
+      t = p.qsl[s];
       const int np = (ctx + 15) >> 4;
       n = ctx > 0 ? (np + p.split_pages - 1) / p.split_pages : 0;
     }
     int total;
     const int ex = block_exclusive_scan(n, sh, total) + carry;
     if (s < p.num_decodes) p.dec_first[s] = ex;
-    for (int k = 0; k < n && ex + k < p.dec_cap; ++k) p.dec_items[ex + k] = make_int2(s, k);
+    for (int k = 0; k < n && ex + k < p.dec_cap; ++k) p.dec_items[ex + k] = make_int4(s, k, ctx, t);
     carry += total;
   }
-  const int dec_total = min(carry, p.dec_cap);
-  carry = 0;
+  for (int i = carry + tid; i < p.dec_cap; i += 1024) p.dec_items[i] = make_int4(-1, 0, 0, 0);
+
+  // prefill tiles and their key splits; heaviest (last) tiles first
+  int tcarry = 0, icarry = 0;
   for (int base = p.num_decodes; base < p.num_seqs; base += 1024) {
     const int s = base + tid;
-    int n = 0;
+    int ntiles = 0, nitems = 0, L = 0, ctx = 0, off = 0;
     if (s < p.num_seqs) {
-      const int L = p.qsl[s + 1] - p.qsl[s];
-      n = L > 0 ? (L * p.G + PF_ROWS - 1) / PF_ROWS : 0;
+      L = p.qsl[s + 1] - p.qsl[s];
+      ctx = p.ctx_lens[s];
+      off = p.q_off[s];
+      ntiles = L > 0 ? (L * p.G + PF_ROWS - 1) / PF_ROWS : 0;
+      for (int t = 0; t < ntiles; ++t)
+        nitems += (tile_key_end(t, L, p.G, ctx, off) + p.pf_split_keys - 1) / p.pf_split_keys;
     }
-    int total;
-    const int ex = block_exclusive_scan(n, sh, total) + carry;
-    // longest-running tiles (last rows see the most keys) first
-    for (int k = 0; k < n && ex + k < p.pf_cap; ++k) p.pf_items[ex + k] = make_int2(s, n - 1 - k);
-    carry += total;
+    int ttotal, itotal;
+    const int tex = block_exclusive_scan(ntiles, sh, ttotal) + tcarry;
+    const int iex = block_exclusive_scan(nitems, sh, itotal) + icarry;
+    int it = iex;
+    for (int k = 0; k < ntiles; ++k) {
+      const int t = ntiles - 1 - k;
+      const int ns = (tile_key_end(t, L, p.G, ctx, off) + p.pf_split_keys - 1) / p.pf_split_keys;
+      if (tex + k < p.pf_tile_cap) p.pf_tiles[tex + k] = make_int4(s, t, it, ns);
+      for (int ks = 0; ks < ns; ++ks, ++it)
+        if (it < p.pf_item_cap) p.pf_items[it] = make_int4(s, t, ks, ns);
+    }
+    tcarry += ttotal;
+    icarry += itotal;
   }
-  if (tid == 0) {
-    p.counts[0] = dec_total;
-    p.counts[1] = min(carry, p.pf_cap);
-  }
+  for (int i = tcarry + tid; i < p.pf_tile_cap; i += 1024) p.pf_tiles[i] = make_int4(-1, 0, 0, 0);
+  for (int i = icarry + tid; i < p.pf_item_cap; i += 1024) p.pf_items[i] = make_int4(-1, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,30 +270,27 @@ __device__ __forceinline__ void decode_load(DecodeBuf<D>& B, const Params& p, co
   const uint16_t* vb = p.v_cache + slab * D * 16 + hl * 16 + g * 4;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
-    B.k[c] = ok ? *reinterpret_cast<const uint4*>(kb + 8 * c) : make_uint4(0, 0, 0, 0);
+    B.k[c] = ok ? stream_load(reinterpret_cast<const uint4*>(kb + 8 * c)) : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
-    B.v[t] = ok ? *reinterpret_cast<const uint2*>(vb + t * 256) : make_uint2(0, 0);
+    B.v[t] = ok ? stream_load(reinterpret_cast<const uint2*>(vb + t * 256)) : make_uint2(0, 0);
 }
 
 template <int D>
 __device__ __forceinline__ void decode_compute(const DecodeBuf<D>& B, int pg, int ctx, int g,
                                                const bf16x8 (&qf)[D / 32], floatx4 (&o)[D / 16],
-                                               float& m, float& l, float scale_log2) {
+                                               float& m, float& l, float c) {
   floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(B.k[c]), qf[c], sacc, 0, 0, 0);
-  // lane holds S^T[key 4g + r][head lane % 16]
-  float x[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) x[r] = sacc[r] * scale_log2;
+  for (int cc = 0; cc < D / 32; ++cc)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(B.k[cc]), qf[cc], sacc, 0, 0, 0);
+  // lane holds S^T[key 4g + r][head lane % 16] (raw scores)
+  float x[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
   uint2 vv[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) vv[t] = B.v[t];
-  const int key0 = pg * 16 + 4 * g;
   if (pg * 16 + 16 > ctx) {  // the page that holds the context end
-    const int n = ctx - key0;  // valid keys among this lane's 4
+    const int n = ctx - (pg * 16 + 4 * g);  // valid keys among this lane's 4
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = (r < n) ? x[r] : -INFINITY;
 #pragma unroll
@@ -219,62 +302,72 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D>& B, int pg, in
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(m, mx);
-  const float alpha = fast_exp2(m - mnew);
+  if ((mx - m) * c > CB_RESCALE_SLACK) {  // raise the running max (per head column)
+    const float alpha = fast_exp2((m - mx) * c);  // m = -inf -> 0
+    l *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) o[t] *= alpha;
+    m = mx;
+  }
+  const float nm = neg_scaled(m, c);
   float pr[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(x[r] - mnew);
-  l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(x[r], c, nm));
+  l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   const uint2 pk = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    o[t] *= alpha;
+  for (int t = 0; t < D / 16; ++t)
     o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv[t]), as_short4(pk), o[t], 0, 0, 0);
-  }
-  m = mnew;
 }
 
 template <int D>
 __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int kvh = w % p.hkv;
   const int j = w / p.hkv;
-  if (j >= p.counts[0]) return;
-  const int2 item = p.dec_items[j];
-  const int s = item.x, split = item.y;
+  if (j >= p.dec_cap) return;
+  const int4 item = p.dec_items[j];
+  if (item.x < 0) return;
+  const int s = item.x, split = item.y, ctx = item.z, t = item.w;
   const int lane = threadIdx.x & 63;
   const int hl = lane & 15, g = lane >> 4;
   const int G = p.G;
-  const int ctx = p.ctx_lens[s];
   const int npages = (ctx + 15) >> 4;
   const int pg0 = split * p.split_pages;
   const int pg1 = min(pg0 + p.split_pages, npages);
   const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
-  const int t = p.qsl[s];
   constexpr int DQ = D / 4;
+  const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+
+  // ring of NB page buffers: page pg+PF is loading while page pg is computed
+  constexpr int PF = CB_DEC_PREFETCH;
+  constexpr int NB = PF + 1;
+  DecodeBuf<D> buf[NB];
+#pragma unroll
+  for (int r = 0; r < PF; ++r)
+    if (pg0 + r < pg1) decode_load<D>(buf[r], p, btrow, pg0 + r, kvh, hl, g);
 
   bf16x8 qf[D / 32];
   {
     const uint16_t* qrow = p.q + ((size_t)t * p.hq + kvh * G + hl) * D + g * DQ;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      qf[c] = as_bf16x8(hl < G ? *reinterpret_cast<const uint4*>(qrow + 8 * c) : make_uint4(0, 0, 0, 0));
+    for (int cc = 0; cc < D / 32; ++cc)
+      qf[cc] = as_bf16x8(hl < G ? *reinterpret_cast<const uint4*>(qrow + 8 * cc) : make_uint4(0, 0, 0, 0));
   }
   floatx4 o[D / 16];
 #pragma unroll
   for (int tt = 0; tt < D / 16; ++tt) o[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
-  const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+  const float c = p.scale_log2;
 
-  DecodeBuf<D> b0, b1;
-  int pg = pg0;
-  if (pg < pg1) decode_load<D>(b0, p, btrow, pg, kvh, hl, g);
-  for (; pg + 1 < pg1; pg += 2) {
-    decode_load<D>(b1, p, btrow, pg + 1, kvh, hl, g);
-    decode_compute<D>(b0, pg, ctx, g, qf, o, m, l, p.scale_log2);
-    if (pg + 2 < pg1) decode_load<D>(b0, p, btrow, pg + 2, kvh, hl, g);
-    decode_compute<D>(b1, pg + 1, ctx, g, qf, o, m, l, p.scale_log2);
+  for (int pg = pg0; pg < pg1; pg += NB) {
+#pragma unroll
+    for (int r = 0; r < NB; ++r) {
+      const int cur = pg + r;
+      if (cur >= pg1) break;
+      if (cur + PF < pg1) decode_load<D>(buf[(r + PF) % NB], p, btrow, cur + PF, kvh, hl, g);
+      decode_compute<D>(buf[r], cur, ctx, g, qf, o, m, l, c);
+    }
   }
-  if (pg < pg1) decode_compute<D>(b0, pg, ctx, g, qf, o, m, l, p.scale_log2);
 
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -290,24 +383,81 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
     }
   } else {
     const size_t prow = (size_t)w * G + hl;
-    float* po = p.part_o + prow * D;
+    float* po = p.dec_o + prow * D;
 #pragma unroll
     for (int tt = 0; tt < D / 16; ++tt) *reinterpret_cast<floatx4*>(po + 16 * tt + 4 * g) = o[tt];
-    if (g == 0) p.part_ml[prow] = make_float2(m, l);
+    if (g == 0) p.dec_ml[prow] = make_float2(m, l);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: one workgroup per (sequence, KV head, 128-row tile).
+// Prefill: one workgroup per (sequence, KV head, 128-row tile, key split).
 // ---------------------------------------------------------------------------
+template <int D>
+struct PfStage {            // one thread's share of one 64-key K/V tile
+  uint4 k[D / 32];
+  uint4 v[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int32_t* btrow, int kt,
+                                         int npages, int ctx, int kvh, int tid) {
+  // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int e = tid + 256 * i;
+    const int pgl = e / (2 * D), rem = e % (2 * D);
+    const int pg = kt * 4 + pgl;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (pg < npages) {
+      const int phys = btrow[pg];
+      if ((unsigned)phys < (unsigned)p.num_pages) {
+        const size_t slab = (size_t)phys * p.hkv + kvh;
+        const int r = rem / (D / 8), c16 = rem % (D / 8);
+        kv = *reinterpret_cast<const uint4*>(p.k_cache + (slab * 16 + r) * D + c16 * 8);
+        const int dr = rem >> 1, hf = rem & 1;
+        vv = *reinterpret_cast<const uint4*>(p.v_cache + (slab * D + dr) * 16 + hf * 8);
+        const int n = ctx - (pg * 16 + hf * 8);  // valid tokens among these 8
+        if (n < 8) {
+          vv.x = keep16(vv.x, 0, n);
+          vv.y = keep16(vv.y, 2, n);
+          vv.z = keep16(vv.z, 4, n);
+          vv.w = keep16(vv.w, 6, n);
+        }
+      }
+    }
+    st.k[i] = kv;
+    st.v[i] = vv;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, int tid) {
+  using Lds = PfLds<D>;
+  uint8_t* kl = stage;
+  uint8_t* vl = stage + Lds::K_BYTES;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const int e = tid + 256 * i;
+    const int pgl = e / (2 * D), rem = e % (2 * D);
+    const int r = rem / (D / 8), c16 = rem % (D / 8);
+    *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = st.k[i];
+    const int dr = rem >> 1, hf = rem & 1;
+    uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(st.v[i].x, st.v[i].y);
+    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(st.v[i].z, st.v[i].w);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* smem) {
   using Lds = PfLds<D>;
   const int kvh = b % p.hkv;
   const int j = b / p.hkv;
-  if (j >= p.counts[1]) return;  // uniform over the workgroup
-  const int2 item = p.pf_items[j];
-  const int s = item.x, tile = item.y;
+  if (j >= p.pf_item_cap) return;
+  const int4 item = p.pf_items[j];  // uniform over the workgroup
+  if (item.x < 0) return;
+  const int s = item.x, tile = item.y, ks = item.z, nsplit = item.w;
   const int G = p.G;
   const int t0 = p.qsl[s];
   const int L = p.qsl[s + 1] - t0;
@@ -324,8 +474,10 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const int hh = row - qi * G;
   const int kcap = min(off + qi, ctx - 1);  // last key this row may see
 
-  const int wg_last_row = min(tile * PF_ROWS + PF_ROWS, R) - 1;
-  const int wg_kend = min(ctx, off + wg_last_row / G + 1);
+  // this item's key range, in whole 64-key tiles
+  const int k_lo = ks * p.pf_split_keys;
+  const int k_hi = min(k_lo + p.pf_split_keys, tile_key_end(tile, L, G, ctx, off));
+  const int kt0 = k_lo / PF_KEYS, kt1 = (k_hi + PF_KEYS - 1) / PF_KEYS;
   const int w_first_row = tile * PF_ROWS + wv * 32;
   const int w_last_row = min(w_first_row + 31, R - 1);
   const int w_kend = (w_first_row < R) ? min(ctx, off + w_last_row / G + 1) : 0;
@@ -333,12 +485,16 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 
   constexpr int NK = D / 16;  // QK k-steps of 16 dims
   constexpr int NO = D / 32;  // 32-dim output tiles
+  const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+  PfStage<D> st;
+  if (kt0 < kt1) pf_fetch<D>(st, p, btrow, kt0, npages, ctx, kvh, tid);
+
   bf16x8 qf[NK];
   {
     const uint16_t* qrow = p.q + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + 8 * gg;
 #pragma unroll
-    for (int c = 0; c < NK; ++c)
-      qf[c] = as_bf16x8(rvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * c) : make_uint4(0, 0, 0, 0));
+    for (int cc = 0; cc < NK; ++cc)
+      qf[cc] = as_bf16x8(rvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
   }
   floatx16 o[NO];
 #pragma unroll
@@ -346,135 +502,119 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m = -INFINITY, l = 0.f;
+  const float c = p.scale_log2;
 
-  const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
-  uint8_t* kl = smem;
-  uint8_t* vl = smem + Lds::K_BYTES;
-  const int ntiles = (wg_kend + PF_KEYS - 1) / PF_KEYS;
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    // stage K: 4 pages x 16 rows x D bf16, 16-byte chunks
-    for (int e = tid; e < 8 * D; e += 256) {
-      const int pgl = e / (2 * D), rem = e % (2 * D);
-      const int r = rem / (D / 8), c16 = rem % (D / 8);
-      const int pg = kt * 4 + pgl;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (pg < npages) {
-        const int phys = btrow[pg];
-        if ((unsigned)phys < (unsigned)p.num_pages)
-          val = *reinterpret_cast<const uint4*>(p.k_cache + (((size_t)phys * p.hkv + kvh) * 16 + r) * D + c16 * 8);
+  if (kt0 < kt1) pf_store<D>(st, smem, tid);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    uint8_t* cur = smem + ((kt - kt0) & 1) * Lds::STAGE;
+    uint8_t* nxt = smem + ((kt - kt0 + 1) & 1) * Lds::STAGE;
+    const bool more = kt + 1 < kt1;
+    if (more) pf_fetch<D>(st, p, btrow, kt + 1, npages, ctx, kvh, tid);
+    const int kbase = kt * PF_KEYS;
+    if (kbase < w_kend) {
+      const uint8_t* kl = cur;
+      const uint8_t* vl = cur + Lds::K_BYTES;
+      // S^T = K Q^T for two 32-key subtiles: lane holds S^T[key 8(r/4)+4gg+r%4][row l32]
+      floatx16 sc[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[sub][r] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NK; ++cc) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + l32) * Lds::KROW + (16 * cc + 8 * gg) * 2);
+          sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[cc], sc[sub], 0, 0, 0);
+        }
       }
-      *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = val;
-    }
-    // stage V: 4 pages x D rows x 16 tokens, 16-byte chunks (8 tokens)
-    for (int e = tid; e < 8 * D; e += 256) {
-      const int pgl = e / (2 * D), rem = e % (2 * D);
-      const int dr = rem >> 1, hf = rem & 1;
-      const int pg = kt * 4 + pgl;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (pg < npages) {
-        const int phys = btrow[pg];
-        if ((unsigned)phys < (unsigned)p.num_pages) {
-          val = *reinterpret_cast<const uint4*>(p.v_cache + (((size_t)phys * p.hkv + kvh) * D + dr) * 16 + hf * 8);
-          const int n = ctx - (pg * 16 + hf * 8);  // valid tokens among these 8
-          if (n < 8) {
-            val.x = keep16(val.x, 0, n);
-            val.y = keep16(val.y, 2, n);
-            val.z = keep16(val.z, 4, n);
-            val.w = keep16(val.w, 6, n);
+      if (kbase + PF_KEYS > w_kfull) {  // straddles this wave's diagonal (or the context end)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * gg + (r & 3);
+            sc[sub][r] = key <= kcap ? sc[sub][r] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool raise = (mx - m) * c > CB_RESCALE_SLACK;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float alpha = raise ? fast_exp2((m - mx) * c) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NO; ++dt) o[dt] *= alpha;
+        m = raise ? mx : m;
+      }
+      const float nm = neg_scaled(m, c);
+      float rs = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(sc[sub][r], c, nm));
+          sc[sub][r] = pv;
+          rs += pv;
+        }
+      l += rs;
+
+      // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int r0 = 8 * half;
+          const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
+                                      pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
+                                      pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
+                                      pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
+          const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
+#pragma unroll
+          for (int dt = 0; dt < NO; ++dt) {
+            const uint8_t* vr = vpage + (32 * dt + l32) * Lds::VROW;
+            const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 8 * gg);
+            const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16 + 8 * gg);
+            const uint4 va = make_uint4(a0.x, a0.y, a1.x, a1.y);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
           }
         }
-      }
-      uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
-      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(val.z, val.w);
     }
+    if (more) pf_store<D>(st, nxt, tid);
     __syncthreads();
-    const int kbase = kt * PF_KEYS;
-    if (kbase >= w_kend) continue;
-
-    // S^T = K Q^T for two 32-key subtiles: lane holds S^T[key 8(r/4)+4gg+r%4][row l32]
-    floatx16 st[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[sub][r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NK; ++c) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + l32) * Lds::KROW + (16 * c + 8 * gg) * 2);
-        st[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[c], st[sub], 0, 0, 0);
-      }
-    }
-    const bool full = kbase + PF_KEYS <= w_kfull;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[sub][r] * p.scale_log2;
-        if (!full) {
-          const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * gg + (r & 3);
-          x = key <= kcap ? x : -INFINITY;
-        }
-        st[sub][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mnew);
-    float rs = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(st[sub][r] - mnew);
-        st[sub][r] = pv;
-        rs += pv;
-      }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < NO; ++dt) o[dt] *= alpha;
-    m = mnew;
-
-    // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile)
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int r0 = 8 * half;
-        const uint4 pb = make_uint4(pack_bf16x2(st[sub][r0 + 0], st[sub][r0 + 1]),
-                                    pack_bf16x2(st[sub][r0 + 2], st[sub][r0 + 3]),
-                                    pack_bf16x2(st[sub][r0 + 4], st[sub][r0 + 5]),
-                                    pack_bf16x2(st[sub][r0 + 6], st[sub][r0 + 7]));
-        const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
-#pragma unroll
-        for (int dt = 0; dt < NO; ++dt) {
-          const uint8_t* vr = vpage + (32 * dt + l32) * Lds::VROW;
-          const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 8 * gg);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16 + 8 * gg);
-          const uint4 va = make_uint4(a0.x, a0.y, a1.x, a1.y);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
-        }
-      }
   }
 
   l += __shfl_xor(l, 32);
   if (!rvalid) return;
-  const float inv = 1.f / l;
-  uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D;
+  if (nsplit == 1) {
+    const float inv = 1.f / l;
+    uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D;
 #pragma unroll
-  for (int dt = 0; dt < NO; ++dt)
+    for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const uint2 v = make_uint2(pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv),
-                                 pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv));
-      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint2 v = make_uint2(pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv),
+                                   pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv));
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
+      }
+  } else {
+    const size_t prow = ((size_t)j * p.hkv + kvh) * PF_ROWS + wv * 32 + l32;
+    float* po = p.pf_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < NO; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<floatx4*>(po + 32 * dt + 8 * q4 + 4 * gg) =
+            floatx4{o[dt][4 * q4 + 0], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+    if (gg == 0) p.pf_ml[prow] = make_float2(m, l);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// The ragged launch: blocks [0, pf_blocks) are prefill tiles, the rest carry
+// The ragged launch: blocks [0, pf_blocks) are prefill items, the rest carry
 // four decode wavefronts each.  The no-prefill instantiation needs neither
 // LDS nor the prefill registers and runs at higher occupancy.
 // ---------------------------------------------------------------------------
@@ -489,17 +629,18 @@ __global__ __launch_bounds__(256, 2) void attn_mixed_kernel(Params p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 3) void attn_decode_kernel(Params p) {
+__global__ __launch_bounds__(256, CB_DEC_WAVES_PER_SIMD) void attn_decode_kernel(Params p) {
   decode_wave<D>(p, (int)blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------------------
-// Split-K combine: one wavefront per (decode sequence, query head).
+// Combine: blocks [0, comb_dec_blocks) merge decode splits, one wavefront per
+// (decode sequence, query head); the rest merge prefill key splits, one
+// workgroup per (row tile, KV head), two threads per row.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(Params p) {
+__device__ void combine_decode(const Params& p, int wave) {
   constexpr int E = D / 64;
-  const int wave = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wave >= p.num_decodes * p.hq) return;
   const int lane = threadIdx.x & 63;
   const int s = wave / p.hq, h = wave % p.hq;
@@ -509,21 +650,37 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p) {
   const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
   if (nsplit <= 1) return;
   const int j0 = p.dec_first[s];
-  if (j0 + nsplit > p.counts[0]) return;  // work list overflowed (precondition broken)
+  if (j0 + nsplit > p.dec_cap) return;  // work list overflowed (precondition broken)
+  const float c = p.scale_log2;
   float M = -INFINITY;
-  for (int i = lane; i < nsplit; i += 64)
-    M = fmaxf(M, p.part_ml[((size_t)(j0 + i) * p.hkv + kvh) * G + hl].x);
+  for (int i = lane; i < nsplit; i += 64) M = fmaxf(M, p.dec_ml[((size_t)(j0 + i) * p.hkv + kvh) * G + hl].x);
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float acc[E], lsum = 0.f;
+  float lsum = 0.f;
+  for (int i = lane; i < nsplit; i += 64) {
+    const float2 ml = p.dec_ml[((size_t)(j0 + i) * p.hkv + kvh) * G + hl];
+    lsum += fast_exp2((ml.x - M) * c) * ml.y;
+  }
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+  float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int i = 0; i < nsplit; ++i) {
-    const size_t prow = ((size_t)(j0 + i) * p.hkv + kvh) * G + hl;
-    const float2 ml = p.part_ml[prow];
-    const float wgt = fast_exp2(ml.x - M);
-    lsum = fmaf(wgt, ml.y, lsum);
+  constexpr int U = 8;
+  for (int i0 = 0; i0 < nsplit; i0 += U) {
+    float mu[U], val[U][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(wgt, p.part_o[prow * D + lane + 64 * e], acc[e]);
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      const size_t prow = ((size_t)(j0 + min(i, nsplit - 1)) * p.hkv + kvh) * G + hl;
+      mu[u] = i < nsplit ? p.dec_ml[prow].x : -INFINITY;
+#pragma unroll
+      for (int e = 0; e < E; ++e) val[u][e] = p.dec_o[prow * D + lane + 64 * e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = fast_exp2((mu[u] - M) * c);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(w, val[u][e], acc[e]);
+    }
   }
   const float inv = 1.f / lsum;
   uint16_t* orow = p.out + ((size_t)p.qsl[s] * p.hq + h) * D;
@@ -532,6 +689,57 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p) {
     const __bf16 v = (__bf16)(acc[e] * inv);
     orow[lane + 64 * e] = __builtin_bit_cast(uint16_t, v);
   }
+}
+
+template <int D>
+__device__ void combine_prefill(const Params& p, int gb) {
+  const int kvh = gb % p.hkv;
+  const int tj = gb / p.hkv;
+  if (tj >= p.pf_tile_cap) return;
+  const int4 tr = p.pf_tiles[tj];
+  if (tr.x < 0 || tr.w <= 1) return;
+  const int s = tr.x, tile = tr.y, first = tr.z, nsplit = tr.w;
+  if (first + nsplit > p.pf_item_cap) return;
+  const int G = p.G;
+  const int t0 = p.qsl[s];
+  const int R = (p.qsl[s + 1] - t0) * G;
+  const int rl = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int row = tile * PF_ROWS + rl;
+  if (row >= R) return;
+  const float c = p.scale_log2;
+  float M = -INFINITY;
+  for (int i = 0; i < nsplit; ++i)
+    M = fmaxf(M, p.pf_ml[((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl].x);
+  float lsum = 0.f;
+  floatx4 acc[D / 8];
+#pragma unroll
+  for (int e = 0; e < D / 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < nsplit; ++i) {
+    const size_t prow = ((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl;
+    const float2 ml = p.pf_ml[prow];
+    const float w = ml.x == -INFINITY ? 0.f : fast_exp2((ml.x - M) * c);
+    lsum = fmaf(w, ml.y, lsum);
+    const floatx4* po = reinterpret_cast<const floatx4*>(p.pf_o + prow * D + half * (D / 2));
+#pragma unroll
+    for (int e = 0; e < D / 8; ++e) acc[e] += w * po[e];
+  }
+  const float inv = 1.f / lsum;
+  const int qi = row / G, hh = row - qi * G;
+  uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + half * (D / 2);
+#pragma unroll
+  for (int e = 0; e < D / 8; ++e) {
+    const uint2 v = make_uint2(pack_bf16x2(acc[e][0] * inv, acc[e][1] * inv),
+                               pack_bf16x2(acc[e][2] * inv, acc[e][3] * inv));
+    *reinterpret_cast<uint2*>(orow + 4 * e) = v;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(Params p) {
+  if ((int)blockIdx.x < p.comb_dec_blocks)
+    combine_decode<D>(p, (int)blockIdx.x * 4 + (threadIdx.x >> 6));
+  else
+    combine_prefill<D>(p, (int)blockIdx.x - p.comb_dec_blocks);
 }
 
 template <int D>
@@ -546,12 +754,14 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
   p.ctx_lens = a.ctx_lens;
   p.q_off = a.q_offsets;
   p.out = static_cast<uint16_t*>(a.out);
-  p.counts = reinterpret_cast<int32_t*>(ws + pl.off_counts);
+  p.dec_items = reinterpret_cast<int4*>(ws + pl.off_dec_items);
+  p.pf_items = reinterpret_cast<int4*>(ws + pl.off_pf_items);
+  p.pf_tiles = reinterpret_cast<int4*>(ws + pl.off_pf_tiles);
   p.dec_first = reinterpret_cast<int32_t*>(ws + pl.off_dec_first);
-  p.dec_items = reinterpret_cast<int2*>(ws + pl.off_dec_items);
-  p.pf_items = reinterpret_cast<int2*>(ws + pl.off_pf_items);
-  p.part_ml = reinterpret_cast<float2*>(ws + pl.off_part_ml);
-  p.part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
+  p.dec_ml = reinterpret_cast<float2*>(ws + pl.off_dec_ml);
+  p.dec_o = reinterpret_cast<float*>(ws + pl.off_dec_o);
+  p.pf_ml = reinterpret_cast<float2*>(ws + pl.off_pf_ml);
+  p.pf_o = reinterpret_cast<float*>(ws + pl.off_pf_o);
   p.bt_stride = a.bt_stride;
   p.num_seqs = a.num_seqs;
   p.num_decodes = a.num_decodes;
@@ -560,12 +770,18 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
   p.G = a.hq / a.hkv;
   p.num_pages = a.num_pages;
   p.split_pages = pl.split_pages;
+  p.pf_split_keys = pl.pf_split_keys;
   p.dec_cap = (int32_t)pl.dec_cap;
-  p.pf_cap = (int32_t)pl.pf_cap;
+  p.pf_tile_cap = (int32_t)pl.pf_tile_cap;
+  p.pf_item_cap = (int32_t)pl.pf_item_cap;
   p.scale_log2 = a.scale * LOG2E;
-  const int64_t pf_blocks = (a.num_seqs > a.num_decodes) ? pl.pf_cap * a.hkv : 0;
+  const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
   const int64_t dec_blocks = (pl.dec_cap * a.hkv + 3) / 4;
   p.pf_blocks = (int32_t)pf_blocks;
+  const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
+  const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
+  const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv : 0;
+  p.comb_dec_blocks = (int32_t)comb_dec;
 
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
@@ -575,10 +791,8 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
     hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((unsigned)dec_blocks), dim3(256), 0, stream, p);
   }
   if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
-  if (a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len) {
-    const int64_t waves = (int64_t)a.num_decodes * a.hq;
-    hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, p);
-  }
+  if (comb_dec + comb_pf > 0)
+    hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)(comb_dec + comb_pf)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -588,24 +802,37 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
                    int32_t head_dim, int32_t max_context_len) {
   Bf16Plan pl{};
   const int64_t max_pages = (max_context_len + 15) / 16;
+  const int64_t G = hkv > 0 ? hq / hkv : 1;
+  // decode: pages per wavefront, so that the decode grid has >= 16k wavefronts
   const int64_t lanes = (int64_t)num_decodes * hkv;
   pl.split_pages = 8;
   for (int sp : {64, 32, 16}) {
     if (lanes * ((max_pages + sp - 1) / sp) >= 16384) { pl.split_pages = sp; break; }
   }
-  const int64_t G = hkv > 0 ? hq / hkv : 1;
   pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);
+  // prefill: row tiles bound by the query tokens; key ranges cut so that about
+  // 1024 workgroups exist when the tiles are long, never below 512 keys
   const int64_t np = num_seqs - num_decodes;
-  pl.pf_cap = np > 0 ? ((int64_t)(num_tokens - num_decodes) * G + PF_ROWS - 1) / PF_ROWS + np : 0;
+  pl.pf_tile_cap = np > 0 ? ((int64_t)(num_tokens - num_decodes) * G + PF_ROWS - 1) / PF_ROWS + np : 0;
+  const int64_t tiles = pl.pf_tile_cap * hkv;
+  int64_t ks = tiles > 0 ? ((int64_t)max_context_len * tiles / 1024 + PF_KEYS - 1) / PF_KEYS * PF_KEYS : PF_KEYS;
+  ks = ks < 512 ? 512 : ks;
+  pl.pf_split_keys = (int32_t)(ks > (int64_t(1) << 30) ? (int64_t(1) << 30) : ks);
+  const int64_t max_splits = (max_context_len + pl.pf_split_keys - 1) / pl.pf_split_keys;
+  pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
+  pl.pf_may_split = max_splits > 1;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 0;
-  pl.off_counts = off;      off = align(off + 2 * sizeof(int32_t));
+  pl.off_dec_items = off;   off = align(off + (size_t)pl.dec_cap * 16);
+  pl.off_pf_items = off;    off = align(off + (size_t)pl.pf_item_cap * 16);
+  pl.off_pf_tiles = off;    off = align(off + (size_t)pl.pf_tile_cap * 16);
   pl.off_dec_first = off;   off = align(off + (size_t)num_decodes * sizeof(int32_t));
-  pl.off_dec_items = off;   off = align(off + (size_t)pl.dec_cap * 8);
-  pl.off_pf_items = off;    off = align(off + (size_t)pl.pf_cap * 8);
-  const size_t nrows = (size_t)pl.dec_cap * hkv * G;
-  pl.off_part_ml = off;     off = align(off + nrows * 8);
-  pl.off_part_o = off;      off = align(off + nrows * head_dim * sizeof(float));
+  const size_t drows = (size_t)pl.dec_cap * hkv * G;
+  pl.off_dec_ml = off;      off = align(off + drows * 8);
+  pl.off_dec_o = off;       off = align(off + drows * head_dim * sizeof(float));
+  const size_t prows = pl.pf_may_split ? (size_t)pl.pf_item_cap * hkv * PF_ROWS : 0;
+  pl.off_pf_ml = off;       off = align(off + prows * 8);
+  pl.off_pf_o = off;        off = align(off + prows * head_dim * sizeof(float));
   pl.bytes = off;
   return pl;
 }

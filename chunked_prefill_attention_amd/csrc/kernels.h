@@ -35,10 +35,14 @@ struct AttnArgs {
 // Sizing of the bf16 path's workspace; a pure function of host scalars so
 // that cb_attention_workspace_bytes and cb_attention_step agree.
 struct Bf16Plan {
-  int32_t split_pages;   // pages per decode wave (split-K unit)
-  int64_t dec_cap;       // bound on (sequence, split) decode items
-  int64_t pf_cap;        // bound on (sequence, 128-row tile) prefill items
-  size_t off_counts, off_dec_first, off_dec_items, off_pf_items, off_part_ml, off_part_o;
+  int32_t split_pages;    // pages per decode wavefront (split-K unit)
+  int32_t pf_split_keys;  // keys per prefill workgroup (split-K unit of a row tile)
+  bool pf_may_split;      // some prefill row tile may need more than one split
+  int64_t dec_cap;        // bound on (sequence, split) decode items
+  int64_t pf_tile_cap;    // bound on (sequence, 128-row tile) prefill tiles
+  int64_t pf_item_cap;    // bound on (tile, key split) prefill items
+  size_t off_dec_items, off_pf_items, off_pf_tiles, off_dec_first;
+  size_t off_dec_ml, off_dec_o, off_pf_ml, off_pf_o;
   size_t bytes;
 };
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
