@@ -154,10 +154,11 @@ class Builder:
     """FIFO batch builder (C++): token budget, request cap, page budget, safety margin."""
 
     def __init__(self, max_batch_tokens, max_requests_per_batch, num_pages, max_prefill_chunk=0,
-                 safety_margin=0.0, page_shuffle_seed=0, _handle=None):
+                 safety_margin=0.0, page_shuffle_seed=0, _handle=None, _owned=True):
         self._lib = load()
+        self._owned = _owned
         if _handle is not None:
-            self._h = _handle
+            self._h = C.c_void_p(_handle) if isinstance(_handle, int) else _handle
             return
         cfg = BuilderConfig(max_batch_tokens, max_requests_per_batch, num_pages, PAGE_SIZE,
                             max_prefill_chunk, safety_margin, page_shuffle_seed)
@@ -172,7 +173,8 @@ class Builder:
 
     def close(self):
         if getattr(self, "_h", None):
-            self._lib.cb_builder_destroy(self._h)
+            if self._owned:
+                self._lib.cb_builder_destroy(self._h)
             self._h = None
 
     __del__ = close

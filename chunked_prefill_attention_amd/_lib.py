@@ -42,6 +42,12 @@ class BuilderStats(C.Structure):
                 ("total_finished", i64), ("fragmentation", C.c_double)]
 
 
+class EngineConfig(C.Structure):
+    _fields_ = [("builder", BuilderConfig), ("num_q_heads", i32), ("num_kv_heads", i32), ("head_dim", i32),
+                ("dtype", i32), ("scale", f32), ("k_cache", vp), ("v_cache", vp), ("meta_device", vp),
+                ("meta_host", vp), ("meta_bytes", sz), ("workspace", vp), ("workspace_bytes", sz)]
+
+
 # name -> (restype, argtypes); one line per declaration of include/cb.h
 SIGNATURES = {
     "cb_status_string": (C.c_char_p, [C.c_int]),
@@ -59,6 +65,15 @@ SIGNATURES = {
     "cb_builder_step": (C.c_int, [vp, C.POINTER(StepDesc)]),
     "cb_builder_block_table": (C.c_int, [vp, i64, P_i32, i32, P_i32]),
     "cb_builder_stats_get": (C.c_int, [vp, C.POINTER(BuilderStats)]),
+    "cb_engine_create": (C.c_int, [C.POINTER(EngineConfig), C.POINTER(vp)]),
+    "cb_engine_destroy": (None, [vp]),
+    "cb_engine_builder": (vp, [vp]),
+    "cb_engine_set_metadata": (C.c_int, [vp, vp, vp, sz]),
+    "cb_engine_set_workspace": (C.c_int, [vp, vp, sz]),
+    "cb_engine_schedule": (C.c_int, [vp, vp, C.POINTER(StepDesc)]),
+    "cb_engine_attend": (C.c_int, [vp, vp, vp, vp, vp, vp]),
+    "cb_engine_workspace_bytes": (sz, [vp]),
+    "cb_engine_load_builder": (C.c_int, [vp, vp]),
 }
 
 _lib = None

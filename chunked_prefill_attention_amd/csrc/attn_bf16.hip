@@ -70,6 +70,10 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_NONTEMPORAL_KV
 #define CB_NONTEMPORAL_KV 0
 #endif
+// threads per workgroup of the decode-only kernel (64 or 256)
+#ifndef CB_DEC_WG
+#define CB_DEC_WG 64
+#endif
 // exponent headroom before the running max is raised (log2 units)
 #ifndef CB_RESCALE_SLACK
 #define CB_RESCALE_SLACK 8.0f
@@ -91,7 +95,8 @@ struct Params {
   int4* dec_items;       // (sequence, split, context length, query row); sequence -1 = no work
   int4* pf_items;        // (sequence, row tile, key split, number of splits); -1 = no work
   int4* pf_tiles;        // (sequence, row tile, first item, number of splits); -1 = none
-  int32_t* dec_first;    // [num_decodes] first decode item of each sequence
+  int32_t* dec_first;    // [num_decodes] first full-length decode item of each sequence
+  int32_t* dec_rem;      // [num_decodes] the sequence's shorter last item, or -1
   float2* dec_ml;        // [decode wave][G] (running max in raw score units, sum)
   float* dec_o;          // [decode wave][G][D] unnormalised
   float2* pf_ml;         // [prefill item][PF_ROWS]
@@ -200,24 +205,55 @@ __device__ __forceinline__ int tile_key_end(int tile, int L, int G, int ctx, int
 __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   __shared__ int sh[40];
   const int tid = threadIdx.x;
-  // decode items: (sequence, split) for every split of every decode sequence
+  // decode items, longest first: every full split (split_pages pages) of every
+  // sequence, then each sequence's shorter last split, by decreasing length.
+  // dec_first[s] = first full split of s; dec_rem[s] = its short split or -1.
+  __shared__ int bucket[65], cursor[65];
+  const int SP = p.split_pages;  // <= 64
+  if (tid <= 64) { bucket[tid] = 0; cursor[tid] = 0; }
+  __syncthreads();
   int carry = 0;
   for (int base = 0; base < p.num_decodes; base += 1024) {
     const int s = base + tid;
-    int n = 0, ctx = 0, t = 0;
+    int nfull = 0, ctx = 0, t = 0, rem = 0;
     if (s < p.num_decodes) {
       ctx = p.ctx_lens[s];
       t = p.qsl[s];
-      const int np = (ctx + 15) >> 4;
-      n = ctx > 0 ? (np + p.split_pages - 1) / p.split_pages : 0;
+      const int np = ctx > 0 ? (ctx + 15) >> 4 : 0;
+      nfull = np / SP;
+      rem = np - nfull * SP;
+      if (rem > 0) atomicAdd(&bucket[SP - rem], 1);
     }
     int total;
-    const int ex = block_exclusive_scan(n, sh, total) + carry;
+    const int ex = block_exclusive_scan(nfull, sh, total) + carry;
     if (s < p.num_decodes) p.dec_first[s] = ex;
-    for (int k = 0; k < n && ex + k < p.dec_cap; ++k) p.dec_items[ex + k] = make_int4(s, k, ctx, t);
+    for (int k = 0; k < nfull && ex + k < p.dec_cap; ++k) p.dec_items[ex + k] = make_int4(s, k, ctx, t);
     carry += total;
   }
-  for (int i = carry + tid; i < p.dec_cap; i += 1024) p.dec_items[i] = make_int4(-1, 0, 0, 0);
+  __syncthreads();
+  if (tid < 64) {  // bucket starts: one wave scans the 64 bucket counts
+    const int n = bucket[tid];
+    bucket[tid] = carry + wave_inclusive_scan(n) - n;
+  }
+  __syncthreads();
+  for (int base = 0; base < p.num_decodes; base += 1024) {
+    const int s = base + tid;
+    if (s < p.num_decodes) {
+      const int ctx = p.ctx_lens[s];
+      const int np = ctx > 0 ? (ctx + 15) >> 4 : 0;
+      const int nfull = np / SP, rem = np - nfull * SP;
+      int idx = -1;
+      if (rem > 0) {
+        idx = bucket[SP - rem] + atomicAdd(&cursor[SP - rem], 1);
+        if (idx < p.dec_cap) p.dec_items[idx] = make_int4(s, nfull, ctx, p.qsl[s]);
+      }
+      p.dec_rem[s] = idx;
+      if (rem > 0) atomicMax(&cursor[64], idx + 1);
+    }
+  }
+  __syncthreads();
+  const int dec_total = max(carry, cursor[64]);
+  for (int i = dec_total + tid; i < p.dec_cap; i += 1024) p.dec_items[i] = make_int4(-1, 0, 0, 0);
 
   // prefill tiles and their key splits; heaviest (last) tiles first
   int tcarry = 0, icarry = 0;
@@ -262,15 +298,16 @@ struct DecodeBuf {
 template <int D>
 __device__ __forceinline__ void decode_load(DecodeBuf<D>& B, const Params& p, const int32_t* btrow,
                                             int pg, int kvh, int hl, int g) {
-  constexpr int DQ = D / 4;
   const int phys = btrow[pg];
   const bool ok = (unsigned)phys < (unsigned)p.num_pages;
   const size_t slab = (size_t)(ok ? phys : 0) * p.hkv + kvh;
-  const uint16_t* kb = p.k_cache + slab * 16 * D + hl * D + g * DQ;
+  // MFMA c takes dims 32c + 8g .. 32c + 8g + 7 from lane group g: the four
+  // groups read 64 contiguous bytes of each key row per load instruction
+  const uint16_t* kb = p.k_cache + slab * 16 * D + hl * D + g * 8;
   const uint16_t* vb = p.v_cache + slab * D * 16 + hl * 16 + g * 4;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c)
-    B.k[c] = ok ? stream_load(reinterpret_cast<const uint4*>(kb + 8 * c)) : make_uint4(0, 0, 0, 0);
+    B.k[c] = ok ? stream_load(reinterpret_cast<const uint4*>(kb + 32 * c)) : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     B.v[t] = ok ? stream_load(reinterpret_cast<const uint2*>(vb + t * 256)) : make_uint2(0, 0);
@@ -335,7 +372,6 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int pg0 = split * p.split_pages;
   const int pg1 = min(pg0 + p.split_pages, npages);
   const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
-  constexpr int DQ = D / 4;
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
 
   // ring of NB page buffers: page pg+PF is loading while page pg is computed
@@ -348,10 +384,10 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
 
   bf16x8 qf[D / 32];
   {
-    const uint16_t* qrow = p.q + ((size_t)t * p.hq + kvh * G + hl) * D + g * DQ;
+    const uint16_t* qrow = p.q + ((size_t)t * p.hq + kvh * G + hl) * D + g * 8;
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc)
-      qf[cc] = as_bf16x8(hl < G ? *reinterpret_cast<const uint4*>(qrow + 8 * cc) : make_uint4(0, 0, 0, 0));
+      qf[cc] = as_bf16x8(hl < G ? *reinterpret_cast<const uint4*>(qrow + 32 * cc) : make_uint4(0, 0, 0, 0));
   }
   floatx4 o[D / 16];
 #pragma unroll
@@ -629,8 +665,8 @@ __global__ __launch_bounds__(256, 2) void attn_mixed_kernel(Params p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, CB_DEC_WAVES_PER_SIMD) void attn_decode_kernel(Params p) {
-  decode_wave<D>(p, (int)blockIdx.x * 4 + (threadIdx.x >> 6));
+__global__ __launch_bounds__(CB_DEC_WG, CB_DEC_WAVES_PER_SIMD) void attn_decode_kernel(Params p) {
+  decode_wave<D>(p, (int)blockIdx.x * (CB_DEC_WG / 64) + (threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -650,14 +686,18 @@ __device__ void combine_decode(const Params& p, int wave) {
   const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
   if (nsplit <= 1) return;
   const int j0 = p.dec_first[s];
-  if (j0 + nsplit > p.dec_cap) return;  // work list overflowed (precondition broken)
+  const int jr = p.dec_rem[s];
+  const int nfull = jr >= 0 ? nsplit - 1 : nsplit;
+  if (j0 + nfull > p.dec_cap || jr >= p.dec_cap) return;  // work list overflowed (precondition broken)
+  // split i lives at item j0 + i (full splits) or jr (the short last split)
+  auto item_of = [&](int i) { return i < nfull ? j0 + i : jr; };
   const float c = p.scale_log2;
   float M = -INFINITY;
-  for (int i = lane; i < nsplit; i += 64) M = fmaxf(M, p.dec_ml[((size_t)(j0 + i) * p.hkv + kvh) * G + hl].x);
+  for (int i = lane; i < nsplit; i += 64) M = fmaxf(M, p.dec_ml[((size_t)item_of(i) * p.hkv + kvh) * G + hl].x);
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float lsum = 0.f;
   for (int i = lane; i < nsplit; i += 64) {
-    const float2 ml = p.dec_ml[((size_t)(j0 + i) * p.hkv + kvh) * G + hl];
+    const float2 ml = p.dec_ml[((size_t)item_of(i) * p.hkv + kvh) * G + hl];
     lsum += fast_exp2((ml.x - M) * c) * ml.y;
   }
   for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
@@ -670,7 +710,7 @@ __device__ void combine_decode(const Params& p, int wave) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u;
-      const size_t prow = ((size_t)(j0 + min(i, nsplit - 1)) * p.hkv + kvh) * G + hl;
+      const size_t prow = ((size_t)item_of(min(i, nsplit - 1)) * p.hkv + kvh) * G + hl;
       mu[u] = i < nsplit ? p.dec_ml[prow].x : -INFINITY;
 #pragma unroll
       for (int e = 0; e < E; ++e) val[u][e] = p.dec_o[prow * D + lane + 64 * e];
@@ -758,6 +798,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
   p.pf_items = reinterpret_cast<int4*>(ws + pl.off_pf_items);
   p.pf_tiles = reinterpret_cast<int4*>(ws + pl.off_pf_tiles);
   p.dec_first = reinterpret_cast<int32_t*>(ws + pl.off_dec_first);
+  p.dec_rem = reinterpret_cast<int32_t*>(ws + pl.off_dec_rem);
   p.dec_ml = reinterpret_cast<float2*>(ws + pl.off_dec_ml);
   p.dec_o = reinterpret_cast<float*>(ws + pl.off_dec_o);
   p.pf_ml = reinterpret_cast<float2*>(ws + pl.off_pf_ml);
@@ -788,7 +829,8 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
   if (pf_blocks > 0) {
     hipLaunchKernelGGL(attn_mixed_kernel<D>, dim3((unsigned)(pf_blocks + dec_blocks)), dim3(256), 0, stream, p);
   } else if (dec_blocks > 0) {
-    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((unsigned)dec_blocks), dim3(256), 0, stream, p);
+    const int64_t blocks = (pl.dec_cap * a.hkv + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64);
+    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((unsigned)blocks), dim3(CB_DEC_WG), 0, stream, p);
   }
   if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
   if (comb_dec + comb_pf > 0)
@@ -827,6 +869,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   pl.off_pf_items = off;    off = align(off + (size_t)pl.pf_item_cap * 16);
   pl.off_pf_tiles = off;    off = align(off + (size_t)pl.pf_tile_cap * 16);
   pl.off_dec_first = off;   off = align(off + (size_t)num_decodes * sizeof(int32_t));
+  pl.off_dec_rem = off;     off = align(off + (size_t)num_decodes * sizeof(int32_t));
   const size_t drows = (size_t)pl.dec_cap * hkv * G;
   pl.off_dec_ml = off;      off = align(off + drows * 8);
   pl.off_dec_o = off;       off = align(off + drows * head_dim * sizeof(float));

@@ -331,3 +331,29 @@ int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out) {
 }
 
 }  // extern "C"
+
+namespace cb {
+int builder_assign(cb_builder* dst, const cb_builder* src) {
+  if (!dst || !src) return fail(CB_ERR_INVALID, "builder_assign: null argument");
+  if (dst == src) return CB_OK;
+  dst->cfg = src->cfg;
+  dst->free_list = src->free_list;
+  dst->arrivals = src->arrivals;
+  dst->steps = src->steps;
+  dst->total_stalls = src->total_stalls;
+  dst->total_finished = src->total_finished;
+  dst->reqs.clear();
+  dst->by_id.clear();
+  for (const auto& r : src->reqs) {
+    dst->reqs.emplace_back(new Request(*r));
+    dst->by_id[r->id] = dst->reqs.back().get();
+  }
+  return CB_OK;
+}
+
+int32_t builder_max_pages_held(const cb_builder* b) {
+  size_t m = 0;
+  for (const auto& r : b->reqs) m = std::max(m, r->pages.size());
+  return (int32_t)m;
+}
+}  // namespace cb

@@ -41,7 +41,7 @@ struct Bf16Plan {
   int64_t dec_cap;        // bound on (sequence, split) decode items
   int64_t pf_tile_cap;    // bound on (sequence, 128-row tile) prefill tiles
   int64_t pf_item_cap;    // bound on (tile, key split) prefill items
-  size_t off_dec_items, off_pf_items, off_pf_tiles, off_dec_first;
+  size_t off_dec_items, off_pf_items, off_pf_tiles, off_dec_first, off_dec_rem;
   size_t off_dec_ml, off_dec_o, off_pf_ml, off_pf_o;
   size_t bytes;
 };

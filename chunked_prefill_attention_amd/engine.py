@@ -1,4 +1,4 @@
-"""One attention layer's engine step: builder -> metadata upload -> append -> attention.
+"""One attention layer's engine step, driven by the native ``cb_engine``.
 
 Hugging Face transformers, "Continuous batching architecture" ("Request
 lifecycle", "Scheduler"): every generation step the scheduler picks the
@@ -6,123 +6,176 @@ requests and tokens of the next forward pass; AI Engineering from Scratch,
 "vLLM serving internals" ("What the scheduler looks like"): the chosen
 decode tokens and prefill chunks then run as one fused GPU call.
 
-``PagedAttentionLayer`` owns the paged K/V caches of one layer, the C++ FIFO
-builder, a pinned host staging buffer and the device workspace.  A step is
+``PagedAttentionLayer`` owns (as torch tensors) the paged K/V caches of one
+layer, two pinned-host and two device metadata slots and the workspace; the
+C++ engine owns the FIFO builder.  A step is two library calls:
 
-    desc = layer.schedule()                 # host: C++ builder
-    meta = layer.upload(desc)               # one async H2D copy of all int32 metadata
-    out  = layer.forward(meta, q, k_new, v_new)   # cb_kv_append + cb_attention_step
+    desc = layer.schedule()                   # builder + packed async upload
+    out  = layer.attend(q, k_new, v_new)      # cb_kv_append + cb_attention_step
 
-All compute runs in the HIP library; this module only moves buffers.
+All compute runs in the HIP library; this module only hands over buffers.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+import ctypes as C
 
 import numpy as np
 
-from . import Builder, Step, attention_step, attention_workspace_bytes, kv_append, CB_BF16, CB_F32, PAGE_SIZE
+from . import Builder, Step, kv_append, CB_BF16, CB_F32, PAGE_SIZE
+from ._lib import BuilderConfig, EngineConfig, StepDesc, CbError, check, load, CB_ERR_CAPACITY, CB_ERR_WORKSPACE
 
 
-@dataclass
-class DeviceStep:
-    """Device views of one step descriptor (int32), plus host scalars."""
-    desc: Step
-    query_start_loc: "object"
-    context_lens: "object"
-    q_offsets: "object"
-    block_tables: "object"
-    slot_mapping: "object"
+def _arr(ptr, n, dtype):
+    if n == 0:
+        return np.zeros(0, dtype)
+    return np.ctypeslib.as_array(ptr, shape=(n,)).copy().astype(dtype, copy=False)
+
+
+class StepView:
+    """The scheduled step: scalars at once, host arrays copied on first use.
+
+    The arrays live in the engine's builder until the next ``schedule``; a
+    view read after that raises instead of returning the next step's data.
+    ``copy()`` returns a view that stays valid.
+    """
+
+    def __init__(self, d: StepDesc, layer=None):
+        self._d = d
+        self._layer = layer
+        self._gen = layer._gen if layer is not None else None
+        self.num_seqs, self.num_decodes, self.num_tokens = d.num_seqs, d.num_decodes, d.num_tokens
+        self.max_query_len, self.max_context_len = d.max_query_len, d.max_context_len
+        self.block_table_stride, self.new_pages = d.block_table_stride, d.new_pages
+        self._cache = {}
+
+    def _get(self, name, n, dtype):
+        if name not in self._cache:
+            if self._layer is not None and self._layer._gen != self._gen:
+                raise RuntimeError("step descriptor read after the next schedule()")
+            self._cache[name] = _arr(getattr(self._d, name), n, dtype)
+        return self._cache[name]
+
+    def copy(self) -> "StepView":
+        for name, n, dt in (("req_ids", self.num_seqs, np.int64), ("query_start_loc", self.num_seqs + 1, np.int32),
+                            ("context_lens", self.num_seqs, np.int32), ("q_offsets", self.num_seqs, np.int32),
+                            ("slot_mapping", self.num_tokens, np.int32),
+                            ("block_tables", self.num_seqs * self.block_table_stride, np.int32),
+                            ("finished_ids", self._d.num_finished, np.int64),
+                            ("stalled_ids", self._d.num_stalled, np.int64)):
+            self._get(name, n, dt)
+        v = StepView.__new__(StepView)
+        v.__dict__.update(self.__dict__)
+        v._cache = dict(self._cache)
+        v._layer = None
+        return v
+
+    req_ids = property(lambda self: self._get("req_ids", self.num_seqs, np.int64))
+    query_start_loc = property(lambda self: self._get("query_start_loc", self.num_seqs + 1, np.int32))
+    context_lens = property(lambda self: self._get("context_lens", self.num_seqs, np.int32))
+    q_offsets = property(lambda self: self._get("q_offsets", self.num_seqs, np.int32))
+    slot_mapping = property(lambda self: self._get("slot_mapping", self.num_tokens, np.int32))
+    finished_ids = property(lambda self: self._get("finished_ids", self._d.num_finished, np.int64))
+    stalled_ids = property(lambda self: self._get("stalled_ids", self._d.num_stalled, np.int64))
+
+    @property
+    def block_tables(self):
+        return self._get("block_tables", self.num_seqs * self.block_table_stride,
+                         np.int32).reshape(self.num_seqs, self.block_table_stride)
+
+    @property
+    def q_lens(self):
+        return np.diff(self.query_start_loc)
 
 
 class PagedAttentionLayer:
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, num_pages: int,
                  max_batch_tokens: int, max_requests_per_batch: int, dtype: str = "bf16",
                  max_prefill_chunk: int = 0, safety_margin: float = 0.0, page_shuffle_seed: int = 0,
-                 device=None, cache_fill: float = 0.0, staging_slots: int = 2):
+                 device=None, cache_fill: float = 0.0, meta_pages_per_request: int = 2048):
         import torch
         self.torch = torch
+        self._lib = load()
         self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_dim
         self.num_pages = num_pages
         self.tdtype = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
         self.code = CB_BF16 if dtype == "bf16" else CB_F32
         self.device = device if device is not None else torch.device("cuda", torch.cuda.current_device())
-        self.builder = Builder(max_batch_tokens, max_requests_per_batch, num_pages, max_prefill_chunk,
-                               safety_margin, page_shuffle_seed)
         self.k_cache = torch.full((num_pages, num_kv_heads, PAGE_SIZE, head_dim), cache_fill,
                                   dtype=self.tdtype, device=self.device)
         self.v_cache = torch.full((num_pages, num_kv_heads, head_dim, PAGE_SIZE), cache_fill,
                                   dtype=self.tdtype, device=self.device)
         self.scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+        B, T = max_requests_per_batch, max_batch_tokens
+        slot_ints = 3 * B + 1 + T + B * min(num_pages, meta_pages_per_request) + 64
+        self._alloc_meta(2 * slot_ints)
         self._ws = None
-        self._staging = [None] * staging_slots   # (pinned host buffer, device buffer) pairs
-        self._slot = 0
+        cfg = EngineConfig(BuilderConfig(max_batch_tokens, max_requests_per_batch, num_pages, PAGE_SIZE,
+                                         max_prefill_chunk, safety_margin, page_shuffle_seed),
+                           num_q_heads, num_kv_heads, head_dim, self.code, self.scale,
+                           self.k_cache.data_ptr(), self.v_cache.data_ptr(), self._meta_dev.data_ptr(),
+                           self._meta_host.data_ptr(), self._meta_dev.numel() * 4, None, 0)
+        h = C.c_void_p()
+        check(self._lib.cb_engine_create(C.byref(cfg), C.byref(h)))
+        self._h = h
+        self.builder = Builder(0, 0, 0, _handle=self._lib.cb_engine_builder(h), _owned=False)
+        self._desc = StepDesc()
+        self._gen = 0
 
-    # -- a1: batch build on the host --------------------------------------------------
-    def schedule(self) -> Step:
-        return self.builder.step()
-
-    # -- a2: metadata upload -------------------------------------------------------------
-    def upload(self, desc: Step, stream=None) -> DeviceStep:
-        """Pack every int32 array of the descriptor and copy it in one transfer.
-
-        Staging buffers rotate so the host can pack step N+1 while step N's
-        copy is still in flight on ``stream``.
-        """
+    def _alloc_meta(self, ints):
         torch = self.torch
-        parts = [desc.query_start_loc, desc.context_lens, desc.q_offsets,
-                 desc.block_tables.reshape(-1), desc.slot_mapping]
-        sizes = [p.size for p in parts]
-        total = int(sum(sizes))
-        slot = self._slot
-        self._slot = (slot + 1) % len(self._staging)
-        buf = self._staging[slot]
-        if buf is not None:
-            buf[2].synchronize()      # the copy that last read this host buffer has finished
-        if buf is None or buf[0].numel() < total:
-            n = max(total, 1 << 16)
-            host = torch.empty(n, dtype=torch.int32, pin_memory=True)
-            devb = torch.empty(n, dtype=torch.int32, device=self.device)
-            buf = self._staging[slot] = (host, devb, torch.cuda.Event())
-        host, devb, done = buf
-        hv = host.numpy()
-        off = 0
-        for p, n in zip(parts, sizes):
-            hv[off:off + n] = p
-            off += n
-        s = stream if stream is not None else torch.cuda.current_stream(self.device)
-        with torch.cuda.stream(s):
-            devb[:total].copy_(host[:total], non_blocking=True)
-            done.record(s)
-        views, off = [], 0
-        for n in sizes:
-            views.append(devb[off:off + n])
-            off += n
-        qsl, ctx, qo, bt, sm = views
-        return DeviceStep(desc, qsl, ctx, qo, bt.view(desc.num_seqs, desc.block_table_stride), sm)
+        self._meta_host = torch.empty(ints, dtype=torch.int32, pin_memory=True)
+        self._meta_dev = torch.empty(ints, dtype=torch.int32, device=self.device)
 
-    def workspace(self, desc: Step):
-        need = attention_workspace_bytes(desc.num_seqs, desc.num_decodes, desc.num_tokens, self.hq,
-                                         self.hkv, self.d, max(desc.max_context_len, 1), self.code)
-        if need and (self._ws is None or self._ws.numel() < need):
-            self._ws = self.torch.empty(int(need * 1.25), dtype=self.torch.uint8, device=self.device)
-        return self._ws if need else None
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.cb_engine_destroy(self._h)
+            self._h = None
 
-    # -- a3..a7: append + attention -------------------------------------------------------
-    def forward(self, meta: DeviceStep, q, k_new, v_new, out=None, stream=None):
-        d = meta.desc
-        if d.num_tokens == 0:
-            return q
-        kv_append(k_new, v_new, self.k_cache, self.v_cache, meta.slot_mapping, stream=stream)
-        return attention_step(q, self.k_cache, self.v_cache, meta.block_tables, meta.query_start_loc,
-                              meta.context_lens, meta.q_offsets, d.num_decodes, d.max_context_len,
-                              self.scale, out=out, workspace=self.workspace(d), stream=stream)
+    __del__ = close
+
+    def _stream(self, stream):
+        s = stream if stream is not None else self.torch.cuda.current_stream(self.device)
+        return C.c_void_p(s.cuda_stream)
+
+    # -- a1 + a2: builder step and metadata upload -----------------------------------------
+    def schedule(self, stream=None) -> StepView:
+        self._gen += 1
+        self._desc = StepDesc()
+        st = self._lib.cb_engine_schedule(self._h, self._stream(stream), C.byref(self._desc))
+        for _ in range(32):
+            if st != CB_ERR_CAPACITY:
+                break
+            # grow the metadata slots (the builder state is unchanged), schedule again
+            self.torch.cuda.synchronize(self.device)
+            self._alloc_meta(2 * self._meta_dev.numel())
+            check(self._lib.cb_engine_set_metadata(self._h, self._meta_dev.data_ptr(),
+                                                   self._meta_host.data_ptr(), self._meta_dev.numel() * 4))
+            st = self._lib.cb_engine_schedule(self._h, self._stream(stream), C.byref(self._desc))
+        check(st)
+        return StepView(self._desc, self)
+
+    # -- a3 .. a7: append + attention --------------------------------------------------------
+    def attend(self, q, k_new, v_new, out=None, stream=None):
+        if out is None:
+            out = self.torch.empty_like(q)
+        args = (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), self._stream(stream))
+        st = self._lib.cb_engine_attend(self._h, *args)
+        if st == CB_ERR_WORKSPACE:
+            need = self._lib.cb_engine_workspace_bytes(self._h)
+            self._ws = self.torch.empty(int(need * 1.25) + 256, dtype=self.torch.uint8, device=self.device)
+            check(self._lib.cb_engine_set_workspace(self._h, self._ws.data_ptr(), self._ws.numel()))
+            st = self._lib.cb_engine_attend(self._h, *args)
+        check(st)
+        return out
+
+    def load_builder(self, snapshot: Builder) -> None:
+        """Restore the scheduler state from a builder snapshot (``Builder.clone()``)."""
+        check(self._lib.cb_engine_load_builder(self._h, snapshot._h))
 
     def write_positions(self, req_pages: np.ndarray, start: int, end: int, k_rows, v_rows, stream=None):
         """Write K/V rows of logical positions start..end-1 of a request whose
         block table is ``req_pages`` (used to import in-flight requests)."""
-        torch = self.torch
         pos = np.arange(start, end)
         slots = (req_pages[pos // PAGE_SIZE].astype(np.int64) * PAGE_SIZE + pos % PAGE_SIZE).astype(np.int32)
-        sm = torch.from_numpy(slots).to(self.device, non_blocking=False)
+        sm = self.torch.from_numpy(slots).to(self.device)
         kv_append(k_rows, v_rows, self.k_cache, self.v_cache, sm, stream=stream)

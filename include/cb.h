@@ -293,6 +293,86 @@ int cb_builder_block_table(const cb_builder* b, int64_t req_id, int32_t* out, in
 
 int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out);
 
+
+/* ----------------------------------------------------------------------------
+ * Engine: the whole per-layer step in native code.
+ *
+ * [VLLM] "What the scheduler looks like": each iteration schedules decode
+ * tokens and prefill chunks and runs them as one fused GPU call; [CBA]
+ * "Continuous batching architecture" lists the CPU overhead of batch assembly
+ * and dispatch as per-step cost.  The engine owns a FIFO builder and uses
+ * caller-provided buffers only (it allocates no device or pinned memory):
+ *
+ *   cb_engine_schedule  host: builder step, descriptor written into a pinned
+ *                       staging slot, one async host-to-device copy on
+ *                       `stream` into a device metadata slot;
+ *   cb_engine_attend    device: cb_kv_append of the step's rows, then
+ *                       cb_attention_step, on `stream`.
+ *
+ * Two staging/metadata slots alternate, so the host can schedule step N+1
+ * while step N runs; before reusing a slot the engine waits (on the host) for
+ * the copy that last read it.  All steps of one engine must be enqueued on
+ * one stream.  The caller computes q, k_new, v_new of the scheduled tokens
+ * (rows in the descriptor's order) between the two calls.
+ * ------------------------------------------------------------------------- */
+typedef struct cb_engine cb_engine;
+
+typedef struct {
+  cb_builder_config builder;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;              /* CB_F32 or CB_BF16 */
+  float scale;                /* softmax scale */
+  void* k_cache;              /* device, [builder.num_pages][Hkv][16][D] */
+  void* v_cache;              /* device, [builder.num_pages][Hkv][D][16] */
+  int32_t* meta_device;       /* device int32 buffer, two slots */
+  int32_t* meta_host;         /* pinned host int32 buffer, two slots */
+  size_t meta_bytes;          /* bytes of each of meta_device and meta_host */
+  void* workspace;            /* device, for cb_attention_step (may be NULL) */
+  size_t workspace_bytes;
+} cb_engine_config;
+
+/* Errors: CB_ERR_INVALID (null buffers, bad shapes), CB_ERR_UNSUPPORTED,
+ * CB_ERR_DEVICE (event creation failed). */
+int cb_engine_create(const cb_engine_config* config, cb_engine** out);
+void cb_engine_destroy(cb_engine* e);
+
+/* The engine's builder (owned by the engine): submit requests, read block
+ * tables and stats through the cb_builder_* calls. */
+cb_builder* cb_engine_builder(cb_engine* e);
+
+/* Replace the metadata buffers (e.g. after CB_ERR_CAPACITY).  The caller must
+ * make sure no upload or kernel still uses the old buffers (synchronise the
+ * stream first).  A scheduled step that was not attended is dropped. */
+int cb_engine_set_metadata(cb_engine* e, int32_t* meta_device, int32_t* meta_host, size_t meta_bytes);
+
+/* Replace the workspace (e.g. after CB_ERR_WORKSPACE from cb_engine_attend). */
+int cb_engine_set_workspace(cb_engine* e, void* workspace, size_t workspace_bytes);
+
+/* Schedule one step and enqueue its metadata upload on `stream`.  *out is the
+ * host descriptor (builder-owned arrays, valid until the next schedule).
+ * Errors: CB_ERR_CAPACITY when the step's metadata could exceed one slot
+ * (checked before the builder runs, so the state is unchanged), CB_ERR_DEVICE. */
+int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out);
+
+/* Append the scheduled tokens' K/V and run the attention step on `stream`.
+ * q, out: device [num_tokens][Hq][D]; k_new, v_new: device [num_tokens][Hkv][D].
+ * Errors: CB_ERR_INVALID (no scheduled step), CB_ERR_WORKSPACE (the step needs
+ * more workspace than configured; call again after cb_engine_set_workspace),
+ * and those of cb_kv_append / cb_attention_step. */
+int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void* v_new, void* out,
+                     void* stream);
+
+/* Replace the engine builder's whole state (requests, pages, free list,
+ * counters) with a deep copy of `src` -- a scheduler checkpoint restore.  A
+ * scheduled step that was not attended is dropped.  The handle returned by
+ * cb_engine_builder stays valid. */
+int cb_engine_load_builder(cb_engine* e, const cb_builder* src);
+
+/* Workspace the last scheduled step needs (0 if none). */
+size_t cb_engine_workspace_bytes(const cb_engine* e);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,3 +170,55 @@ def test_bad_page_ids_read_as_zero_pages():
     bad[:, 1] = st.num_pages + 1000
     out = st.run(kc, vc, table=bad)
     assert torch.isfinite(out.float()).all()
+
+
+def test_engine_page_example_with_buffer_growth():
+    """The pages' example through the native engine (schedule + attend), with
+    metadata slots sized to force one CB_ERR_CAPACITY regrowth and a workspace
+    grown on first use."""
+    from chunked_prefill_attention_amd.engine import PagedAttentionLayer
+    q, k, v = wl.page_example_tensors()
+    layer = PagedAttentionLayer(8, 8, 64, 70, 256, 128, "f32", page_shuffle_seed=3, cache_fill=float("nan"),
+                                meta_pages_per_request=0)
+    layer.builder.submit(0, 1000, 1)
+    outs = []
+    while True:
+        d = layer.schedule()
+        if d.num_tokens == 0:
+            break
+        a, e = int(d.q_offsets[0]), int(d.context_lens[0])
+        outs.append(layer.attend(to_dev(q[a:e], "f32"), to_dev(k[a:e], "f32"), to_dev(v[a:e], "f32")).cpu().numpy())
+    compare(np.concatenate(outs), ora.attend(q, k, v, wl.softmax_scale(64)), "f32", "engine page example")
+
+
+def test_engine_mixed_bf16_matches_direct_calls_bitwise():
+    """Engine step == builder + cb_kv_append + cb_attention_step called directly."""
+    from chunked_prefill_attention_amd.engine import PagedAttentionLayer
+    hq, hkv, d = 32, 8, 128
+    reqs = [(900, 5, 899), (300, 5, 299), (1500, 5, 1024), (700, 5, 0)]
+    layer = PagedAttentionLayer(hq, hkv, d, 400, 600, 16, "bf16", page_shuffle_seed=9)
+    ref_b = cb.Builder(600, 16, 400, page_shuffle_seed=9)
+    kc2, vc2 = new_cache(400, hkv, d, "bf16", 0.0)
+    hist = {}
+    for i, (p, o, c) in enumerate(reqs):
+        layer.builder.submit(i, p, o, c)
+        ref_b.submit(i, p, o, c)
+        k, v = wl.seq_kv(31, i, 0, p + o, hkv, d, "bf16")
+        hist[i] = (k, v)
+        if c:
+            layer.write_positions(layer.builder.block_table(i), 0, c, to_dev(k[:c], "bf16"), to_dev(v[:c], "bf16"))
+            write_history(kc2, vc2, k, v, ref_b.block_table(i), 0, c, "bf16")
+    for step in range(3):
+        dsc = layer.schedule().copy()
+        rs = ref_b.step()
+        assert rs.req_ids.tolist() == dsc.req_ids.tolist() and np.array_equal(rs.block_tables, dsc.block_tables)
+        kn = np.concatenate([hist[int(r)][0][a:e] for r, a, e in zip(dsc.req_ids, dsc.q_offsets, dsc.context_lens)])
+        vn = np.concatenate([hist[int(r)][1][a:e] for r, a, e in zip(dsc.req_ids, dsc.q_offsets, dsc.context_lens)])
+        qq = wl.step_q(31, step, dsc.num_tokens, hq, d, "bf16")
+        o1 = layer.attend(to_dev(qq, "bf16"), to_dev(kn, "bf16"), to_dev(vn, "bf16"))
+        cb.kv_append(to_dev(kn, "bf16"), to_dev(vn, "bf16"), kc2, vc2, i32(rs.slot_mapping))
+        o2 = cb.attention_step(to_dev(qq, "bf16"), kc2, vc2, i32(rs.block_tables), i32(rs.query_start_loc),
+                               i32(rs.context_lens), i32(rs.q_offsets), rs.num_decodes, rs.max_context_len,
+                               wl.softmax_scale(d))
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), step

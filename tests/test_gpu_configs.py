@@ -44,7 +44,6 @@ class Run:
     def step(self):
         L, w = self.layer, self.w
         desc = L.schedule()
-        meta = L.upload(desc)
         ks, vs = [], []
         for s in range(desc.num_seqs):
             i = int(desc.req_ids[s])
@@ -52,7 +51,7 @@ class Run:
             ks.append(self.hist[i][0][a:e])
             vs.append(self.hist[i][1][a:e])
         q = wl.step_q(w.seed, self.steps, desc.num_tokens, w.n_q_heads, w.head_dim, w.dtype)
-        out = L.forward(meta, self._dev(q), self._dev(np.concatenate(ks)), self._dev(np.concatenate(vs)))
+        out = L.attend(self._dev(q), self._dev(np.concatenate(ks)), self._dev(np.concatenate(vs)))
         torch.cuda.synchronize()
         self.steps += 1
         return desc, q, out.float().cpu().numpy()
@@ -144,12 +143,11 @@ def test_fifo_trace_every_step():
         if desc.num_tokens == 0:
             step += 1
             continue
-        meta = L.upload(desc)
         T = desc.num_tokens
         kn = wl.device_normal((T, hkv, d), dtype, dev(), 5, step, 1)
         vn = wl.device_normal((T, hkv, d), dtype, dev(), 5, step, 2)
         qd = wl.device_normal((T, hq, d), dtype, dev(), 5, step, 3)
-        out = L.forward(meta, qd, kn, vn)
+        out = L.attend(qd, kn, vn)
         kh = kn.view(torch.int16).cpu().numpy().view(np.uint16)
         vh = vn.view(torch.int16).cpu().numpy().view(np.uint16)
         for s in range(desc.num_seqs):
