@@ -57,6 +57,23 @@ def workload(name):
     raise SystemExit(f"unknown workload {name}")
 
 
+def counted_traffic(workload_name):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3
+    counter runs (FETCH_SIZE / WRITE_SIZE scaled by the copy-kernel
+    calibration), or None when the kernel source changed since they were taken
+    or no record covers this workload."""
+    import glob
+    import hashlib
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+        rec = json.load(open(path))
+        if rec.get("workload") != workload_name:
+            continue
+        src = os.path.join(ROOT, rec["source"])
+        if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == rec["source_sha256"]:
+            return rec["traffic_bytes"]
+    return None
+
+
 def algorithmic(desc, hq, hkv, d, esize):
     """Bytes the step must move and flops it must do (no padding, no re-reads)."""
     import numpy as np
@@ -168,6 +185,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(flops_alg / kern_s / 1e12, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(flops_alg / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = counted_traffic(w.name)
     roof["kernel"] = "attn_mixed_kernel<128>" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel<128>"
     roof["kernel_us"] = round(kern_s * 1e6, 2)
     roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
