@@ -197,7 +197,7 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
     tokens_left -= 1;
     slots_left -= 1;
   }
-  // 2. active prefills, as many tokens as possible
+  // 2. active prefills, each taking every token that still fits
   for (auto& up : b->reqs) {
     Request* r = up.get();
     if (r->state != State::Prefilling) continue;

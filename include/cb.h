@@ -192,8 +192,8 @@ int cb_profile_events(void* start_event, void* stop_event);
  * (max_batch_tokens), the cache budget (KV pages) and the request cap
  * (max_requests_per_batch).  [CBA] "FIFO": active decodes first, then active
  * prefills, then waiting requests in arrival order.  [CBA] "Chunked
- * prefill": a prompt beyond the remaining budget is processed for as many
- * tokens as possible and resumes next step.  [CBA] "Admission": a request that
+ * prefill": a prompt beyond the remaining budget takes every token that
+ * still fits and resumes in the next step.  [CBA] "Admission": a request that
  * cannot be held is not admitted and nothing is allocated; below
  * safety_margin of free pages new prefills wait while active work continues.
  * [VLLM] "What the scheduler looks like": finished requests release their

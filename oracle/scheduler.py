@@ -7,8 +7,8 @@ Follows these passages of the pages:
     FINISHED; it leaves the queue when the scheduler has enough token budget
     and cache room; a prompt too long for one step is split over several
     forward passes.
-  - "Chunked prefill": a prompt that exceeds the remaining token budget is
-    processed for as many tokens as possible; the rest resumes next step
+  - "Chunked prefill": a prompt longer than the remaining token budget takes
+    every token that still fits; the rest resumes in the next step from
     where it stopped.
   - "Scheduler": three limits per forward pass -- the token budget
     (``max_batch_tokens``), the cache budget (KV pages), and the request
@@ -185,7 +185,7 @@ class FifoScheduler:
             tokens_left -= 1
             slots_left -= 1
 
-        # 2. active prefills, as many tokens as possible
+        # 2. active prefills, each taking every token that still fits
         for r in self._ordered(PREFILLING):
             if tokens_left < 1 or slots_left < 1:
                 break
