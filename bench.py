@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--workload", default="mixed", choices=["mixed", "decode", "long", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--page-order", default="shuffled", choices=["shuffled", "sequential"],
+                    help="physical page ids: a seeded random permutation (default) or handed out in order")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -116,7 +118,8 @@ def main():
     hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
     t_setup = time.perf_counter()
     layer = PagedAttentionLayer(hq, hkv, d, w.pool_pages, w.max_batch_tokens, w.max_requests, w.dtype,
-                                w.max_prefill_chunk, w.safety_margin, page_shuffle_seed=w.seed, device=dev)
+                                w.max_prefill_chunk, w.safety_margin,
+                                page_shuffle_seed=w.seed if args.page_order == "shuffled" else 0, device=dev)
     hist = {}
     for i, (p, o, c) in enumerate(w.requests):
         layer.builder.submit(i, p, o, c)
@@ -202,7 +205,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
-        "config": {"workload": w.name, "num_seqs": desc0.num_seqs, "num_decodes": desc0.num_decodes,
+        "config": {"workload": w.name, "page_order": args.page_order, "num_seqs": desc0.num_seqs, "num_decodes": desc0.num_decodes,
                    "num_tokens": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "page_size": 16,
                    "max_batch_tokens": w.max_batch_tokens, "max_context_len": desc0.max_context_len,
                    "kv_bytes_read": bytes_alg, "visible_pairs": pairs, "flops": flops_alg},

@@ -47,6 +47,7 @@
 // the output.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "kernels.h"
@@ -81,6 +82,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int PF_ROWS = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int PF_KEYS = 64;   // keys per prefill tile (4 pages)
+constexpr int PF_MAX_PAGES = 512;                          // page ids one prefill item stages in LDS
+constexpr int PF_MAX_KEYS = (PF_MAX_PAGES - 4) * 16 / PF_KEYS * PF_KEYS;  // largest key range per item
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct Params {
@@ -121,6 +124,7 @@ struct PfLds {
   static constexpr int V_BYTES = (PF_KEYS / 16) * D * VROW;
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int BYTES = 2 * STAGE;  // double buffered
+  static constexpr int TOTAL = BYTES + PF_MAX_PAGES * 4;  // + the item's page ids
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -142,24 +146,31 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // masked scores (-inf) still give exp2(-inf) = 0 instead of NaN.
 __device__ __forceinline__ float neg_scaled(float m, float c) { return m == -INFINITY ? 0.f : -m * c; }
 
-// Streaming loads of K/V pages: each byte is used once per launch.
+// Loads through the global address space (pointers rebuilt from SGPR halves
+// would otherwise become generic "flat" accesses, which the compiler must
+// order against LDS traffic too).  K/V page loads are streaming: each byte is
+// used once per launch.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const u32x2 gu32x2;
 __device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  gu32x4* g = (gu32x4*)p;
 #if CB_NONTEMPORAL_KV
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+  const u32x4 v = __builtin_nontemporal_load(g);
 #else
-  return *p;
+  const u32x4 v = *g;
 #endif
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint2 stream_load(const uint2* p) {
+  gu32x2* g = (gu32x2*)p;
 #if CB_NONTEMPORAL_KV
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v.x, v.y);
+  const u32x2 v = __builtin_nontemporal_load(g);
 #else
-  return *p;
+  const u32x2 v = *g;
 #endif
+  return make_uint2(v.x, v.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,30 +302,41 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct DecodeBuf {
-  uint4 k[D / 32];  // this lane's slice of one K page (one key, D/4 dims)
+  uint4 k[D / 32];  // this lane's slice of one K page (one key, 8 dims per MFMA)
   uint2 v[D / 16];  // this lane's slice of one V page (4 keys for each of D/16 dims)
 };
 
+// A wave-uniform pointer: both halves in SGPRs, so loads use the
+// scalar-base + vector-offset + immediate-offset addressing form.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+// Issue one page's loads.  Every call issues exactly the same loads with
+// constant offsets, so the next pages stay in flight while the current one is
+// computed (a conditional load would make the compiler drain every load at the
+// join).  `phys` is wave-uniform; an id out of range (a broken precondition,
+// or the slots past the end of the split, which are never computed) reads
+// page 0 instead.
 template <int D>
-__device__ __forceinline__ void decode_load(DecodeBuf<D>& B, const Params& p, const int32_t* btrow,
-                                            int pg, int kvh, int hl, int g) {
-  const int phys = btrow[pg];
-  const bool ok = (unsigned)phys < (unsigned)p.num_pages;
-  const size_t slab = (size_t)(ok ? phys : 0) * p.hkv + kvh;
-  // MFMA c takes dims 32c + 8g .. 32c + 8g + 7 from lane group g: the four
-  // groups read 64 contiguous bytes of each key row per load instruction
-  const uint16_t* kb = p.k_cache + slab * 16 * D + hl * D + g * 8;
-  const uint16_t* vb = p.v_cache + slab * D * 16 + hl * 16 + g * 4;
+__device__ __forceinline__ void decode_issue(DecodeBuf<D>& B, const Params& p, int phys, int kvh,
+                                             int koff, int voff) {
+  const int pg = (unsigned)phys < (unsigned)p.num_pages ? phys : 0;
+  const size_t slab = (size_t)pg * p.hkv + kvh;
+  const uint16_t* kb = uniform_ptr(p.k_cache + slab * 16 * D);
+  const uint16_t* vb = uniform_ptr(p.v_cache + slab * D * 16);
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-    B.k[c] = ok ? stream_load(reinterpret_cast<const uint4*>(kb + 32 * c)) : make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < D / 32; ++c) B.k[c] = stream_load(reinterpret_cast<const uint4*>(kb + koff + 32 * c));
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    B.v[t] = ok ? stream_load(reinterpret_cast<const uint2*>(vb + t * 256)) : make_uint2(0, 0);
+  for (int t = 0; t < D / 16; ++t) B.v[t] = stream_load(reinterpret_cast<const uint2*>(vb + voff + 256 * t));
 }
 
 template <int D>
-__device__ __forceinline__ void decode_compute(const DecodeBuf<D>& B, int pg, int ctx, int g,
+__device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx, int g,
                                                const bf16x8 (&qf)[D / 32], floatx4 (&o)[D / 16],
                                                float& m, float& l, float c) {
   floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -323,17 +345,14 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D>& B, int pg, in
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(B.k[cc]), qf[cc], sacc, 0, 0, 0);
   // lane holds S^T[key 4g + r][head lane % 16] (raw scores)
   float x[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
-  uint2 vv[D / 16];
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) vv[t] = B.v[t];
   if (pg * 16 + 16 > ctx) {  // the page that holds the context end
     const int n = ctx - (pg * 16 + 4 * g);  // valid keys among this lane's 4
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = (r < n) ? x[r] : -INFINITY;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      vv[t].x = keep16(vv[t].x, 0, n);
-      vv[t].y = keep16(vv[t].y, 2, n);
+      B.v[t].x = keep16(B.v[t].x, 0, n);
+      B.v[t].y = keep16(B.v[t].y, 2, n);
     }
   }
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -354,7 +373,7 @@ __device__ __forceinline__ void decode_compute(const DecodeBuf<D>& B, int pg, in
   const uint2 pk = make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
-    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv[t]), as_short4(pk), o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(B.v[t]), as_short4(pk), o[t], 0, 0, 0);
 }
 
 template <int D>
@@ -363,8 +382,12 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int j = w / p.hkv;
   if (j >= p.dec_cap) return;
   const int4 item = p.dec_items[j];
-  if (item.x < 0) return;
-  const int s = item.x, split = item.y, ctx = item.z, t = item.w;
+  // the record is the same for the whole wavefront: keep its fields in SGPRs
+  const int s = __builtin_amdgcn_readfirstlane(item.x);
+  if (s < 0) return;
+  const int split = __builtin_amdgcn_readfirstlane(item.y);
+  const int ctx = __builtin_amdgcn_readfirstlane(item.z);
+  const int t = __builtin_amdgcn_readfirstlane(item.w);
   const int lane = threadIdx.x & 63;
   const int hl = lane & 15, g = lane >> 4;
   const int G = p.G;
@@ -373,14 +396,23 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int pg1 = min(pg0 + p.split_pages, npages);
   const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+  // per-lane element offsets inside a (page, head) slab: K row hl, dims 8g + 32c;
+  // V dim rows 16t + hl, keys 4g..4g+3
+  const int koff = hl * D + g * 8;
+  const int voff = hl * 16 + g * 4;
 
+  // this split's physical page ids, one per lane (split_pages <= 64); the wait
+  // for them happens here, before any page load is in flight
+  const int my_page = __builtin_amdgcn_readfirstlane(0) + ((lane < pg1 - pg0) ? btrow[pg0 + lane] : 0);
+  const int first_page = __builtin_amdgcn_readlane(my_page, 0);
   // ring of NB page buffers: page pg+PF is loading while page pg is computed
   constexpr int PF = CB_DEC_PREFETCH;
   constexpr int NB = PF + 1;
   DecodeBuf<D> buf[NB];
+  decode_issue<D>(buf[0], p, pg0 < pg1 ? first_page : -1, kvh, koff, voff);
 #pragma unroll
-  for (int r = 0; r < PF; ++r)
-    if (pg0 + r < pg1) decode_load<D>(buf[r], p, btrow, pg0 + r, kvh, hl, g);
+  for (int r = 1; r < PF; ++r)
+    decode_issue<D>(buf[r], p, pg0 + r < pg1 ? __builtin_amdgcn_readlane(my_page, r) : -1, kvh, koff, voff);
 
   bf16x8 qf[D / 32];
   {
@@ -399,9 +431,11 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
 #pragma unroll
     for (int r = 0; r < NB; ++r) {
       const int cur = pg + r;
-      if (cur >= pg1) break;
-      if (cur + PF < pg1) decode_load<D>(buf[(r + PF) % NB], p, btrow, cur + PF, kvh, hl, g);
-      decode_compute<D>(buf[r], cur, ctx, g, qf, o, m, l, c);
+      const int nxt = cur + PF;
+      // readlane's lane index wraps past 63; the page is then unused (nxt >= pg1)
+      const int phys = nxt < pg1 ? __builtin_amdgcn_readlane(my_page, (nxt - pg0) & 63) : -1;
+      decode_issue<D>(buf[(r + PF) % NB], p, phys, kvh, koff, voff);
+      if (cur < pg1) decode_compute<D>(buf[r], cur, ctx, g, qf, o, m, l, c);
     }
   }
 
@@ -436,31 +470,33 @@ struct PfStage {            // one thread's share of one 64-key K/V tile
 };
 
 template <int D>
-__device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int32_t* btrow, int kt,
-                                         int npages, int ctx, int kvh, int tid) {
-  // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens
+__device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int* pids, int kt, int kt0,
+                                         int ctx, int kvh, int tid) {
+  // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens.
+  // Chunk i of a thread lies in page (tid + 256 i) / 2D of the tile, the same
+  // page for the whole wavefront; its id comes from LDS (-1 = no page).
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const int e = tid + 256 * i;
     const int pgl = e / (2 * D), rem = e % (2 * D);
     const int pg = kt * 4 + pgl;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (pg < npages) {
-      const int phys = btrow[pg];
-      if ((unsigned)phys < (unsigned)p.num_pages) {
-        const size_t slab = (size_t)phys * p.hkv + kvh;
-        const int r = rem / (D / 8), c16 = rem % (D / 8);
-        kv = *reinterpret_cast<const uint4*>(p.k_cache + (slab * 16 + r) * D + c16 * 8);
-        const int dr = rem >> 1, hf = rem & 1;
-        vv = *reinterpret_cast<const uint4*>(p.v_cache + (slab * D + dr) * 16 + hf * 8);
-        const int n = ctx - (pg * 16 + hf * 8);  // valid tokens among these 8
-        if (n < 8) {
-          vv.x = keep16(vv.x, 0, n);
-          vv.y = keep16(vv.y, 2, n);
-          vv.z = keep16(vv.z, 4, n);
-          vv.w = keep16(vv.w, 6, n);
-        }
-      }
+    // pages past the context (id -1) read page 0; their keys are masked by
+    // the causal test and their V tokens zeroed below (n <= 0)
+    const int ph = __builtin_amdgcn_readfirstlane(pids[(kt - kt0) * 4 + pgl]);
+    const int phys = (unsigned)ph < (unsigned)p.num_pages ? ph : 0;
+    const size_t slab = (size_t)phys * p.hkv + kvh;
+    const uint16_t* kb = uniform_ptr(p.k_cache + slab * 16 * D);
+    const uint16_t* vb = uniform_ptr(p.v_cache + slab * D * 16);
+    const int r = rem / (D / 8), c16 = rem % (D / 8);
+    const uint4 kv = stream_load(reinterpret_cast<const uint4*>(kb + r * D + c16 * 8));
+    const int dr = rem >> 1, hf = rem & 1;
+    uint4 vv = stream_load(reinterpret_cast<const uint4*>(vb + dr * 16 + hf * 8));
+    const int n = ctx - (pg * 16 + hf * 8);  // valid tokens among these 8
+    if (n < 8) {
+      vv.x = keep16(vv.x, 0, n);
+      vv.y = keep16(vv.y, 2, n);
+      vv.z = keep16(vv.z, 4, n);
+      vv.w = keep16(vv.w, 6, n);
     }
     st.k[i] = kv;
     st.v[i] = vv;
@@ -492,8 +528,11 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const int j = b / p.hkv;
   if (j >= p.pf_item_cap) return;
   const int4 item = p.pf_items[j];  // uniform over the workgroup
-  if (item.x < 0) return;
-  const int s = item.x, tile = item.y, ks = item.z, nsplit = item.w;
+  const int s = __builtin_amdgcn_readfirstlane(item.x);
+  if (s < 0) return;
+  const int tile = __builtin_amdgcn_readfirstlane(item.y);
+  const int ks = __builtin_amdgcn_readfirstlane(item.z);
+  const int nsplit = __builtin_amdgcn_readfirstlane(item.w);
   const int G = p.G;
   const int t0 = p.qsl[s];
   const int L = p.qsl[s + 1] - t0;
@@ -522,8 +561,15 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   constexpr int NK = D / 16;  // QK k-steps of 16 dims
   constexpr int NO = D / 32;  // 32-dim output tiles
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+  // the item's page ids, staged once (at most PF_MAX_PAGES; the host caps the key range)
+  int* pids = reinterpret_cast<int*>(smem + Lds::BYTES);
+  for (int i = tid; i < (kt1 - kt0) * 4; i += 256) {
+    const int pg = kt0 * 4 + i;
+    pids[i] = pg < npages ? btrow[pg] : -1;
+  }
+  __syncthreads();
   PfStage<D> st;
-  if (kt0 < kt1) pf_fetch<D>(st, p, btrow, kt0, npages, ctx, kvh, tid);
+  if (kt0 < kt1) pf_fetch<D>(st, p, pids, kt0, kt0, ctx, kvh, tid);
 
   bf16x8 qf[NK];
   {
@@ -546,7 +592,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     uint8_t* cur = smem + ((kt - kt0) & 1) * Lds::STAGE;
     uint8_t* nxt = smem + ((kt - kt0 + 1) & 1) * Lds::STAGE;
     const bool more = kt + 1 < kt1;
-    if (more) pf_fetch<D>(st, p, btrow, kt + 1, npages, ctx, kvh, tid);
+    if (more) pf_fetch<D>(st, p, pids, kt + 1, kt0, ctx, kvh, tid);
     const int kbase = kt * PF_KEYS;
     if (kbase < w_kend) {
       const uint8_t* kl = cur;
@@ -656,7 +702,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_mixed_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
   if ((int)blockIdx.x < p.pf_blocks) {
     prefill_tile<D>(p, blockIdx.x, smem);
     return;
@@ -783,7 +829,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Params p) {
 }
 
 template <int D>
-hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
+hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* lists, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   Params p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -824,7 +870,15 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
   const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv : 0;
   p.comb_dec_blocks = (int32_t)comb_dec;
 
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  if (lists) {  // built by the caller: read them where they were uploaded
+    p.dec_items = const_cast<int4*>(static_cast<const int4*>(lists->dec_items));
+    p.pf_items = const_cast<int4*>(static_cast<const int4*>(lists->pf_items));
+    p.pf_tiles = const_cast<int4*>(static_cast<const int4*>(lists->pf_tiles));
+    p.dec_first = const_cast<int32_t*>(lists->dec_first);
+    p.dec_rem = const_cast<int32_t*>(lists->dec_rem);
+  } else {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  }
   if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
   if (pf_blocks > 0) {
     hipLaunchKernelGGL(attn_mixed_kernel<D>, dim3((unsigned)(pf_blocks + dec_blocks)), dim3(256), 0, stream, p);
@@ -859,7 +913,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t tiles = pl.pf_tile_cap * hkv;
   int64_t ks = tiles > 0 ? ((int64_t)max_context_len * tiles / 1024 + PF_KEYS - 1) / PF_KEYS * PF_KEYS : PF_KEYS;
   ks = ks < 512 ? 512 : ks;
-  pl.pf_split_keys = (int32_t)(ks > (int64_t(1) << 30) ? (int64_t(1) << 30) : ks);
+  pl.pf_split_keys = (int32_t)(ks > PF_MAX_KEYS ? PF_MAX_KEYS : ks);
   const int64_t max_splits = (max_context_len + pl.pf_split_keys - 1) / pl.pf_split_keys;
   pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
   pl.pf_may_split = max_splits > 1;
@@ -880,10 +934,79 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   return pl;
 }
 
-hipError_t launch_attention_bf16(const AttnArgs& a, const Bf16Plan& pl, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_d<128>(a, pl, stream);
-  if (a.head_dim == 64) return launch_d<64>(a, pl, stream);
+hipError_t launch_attention_bf16(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* lists,
+                                 hipStream_t stream) {
+  if (a.head_dim == 128) return launch_d<128>(a, pl, lists, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, pl, lists, stream);
   return hipErrorInvalidValue;
+}
+
+WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
+  auto align = [](size_t x) { return (x + 15) & ~size_t(15); };
+  WorkListLayout L{};
+  size_t off = 0;
+  L.dec_items = off;  off = align(off + (size_t)pl.dec_cap * 16);
+  L.pf_items = off;   off = align(off + (size_t)pl.pf_item_cap * 16);
+  L.pf_tiles = off;   off = align(off + (size_t)pl.pf_tile_cap * 16);
+  L.dec_first = off;  off = align(off + (size_t)num_decodes * 4);
+  L.dec_rem = off;    off = align(off + (size_t)num_decodes * 4);
+  L.bytes = off;
+  return L;
+}
+
+// Mirrors plan_kernel: decode items longest first (every full split, then the
+// short last splits by decreasing length, sequences in order within a
+// length), prefill tiles heaviest (last) first with their key splits.
+void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G,
+                      const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst) {
+  const WorkListLayout L = work_list_layout(pl, num_decodes);
+  uint8_t* base = static_cast<uint8_t*>(dst);
+  int4* dec = reinterpret_cast<int4*>(base + L.dec_items);
+  int4* pfi = reinterpret_cast<int4*>(base + L.pf_items);
+  int4* pft = reinterpret_cast<int4*>(base + L.pf_tiles);
+  int32_t* first = reinterpret_cast<int32_t*>(base + L.dec_first);
+  int32_t* rem_at = reinterpret_cast<int32_t*>(base + L.dec_rem);
+  const int SP = pl.split_pages;
+  int64_t n = 0;
+  int counts[65] = {0};
+  for (int s = 0; s < num_decodes; ++s) {
+    const int np = ctx[s] > 0 ? (ctx[s] + 15) >> 4 : 0;
+    const int nfull = np / SP, rem = np - nfull * SP;
+    first[s] = (int32_t)n;
+    for (int k = 0; k < nfull && n < pl.dec_cap; ++k) dec[n++] = make_int4(s, k, ctx[s], qsl[s]);
+    if (rem > 0) counts[SP - rem]++;
+  }
+  int starts[65];
+  for (int b = 0, acc = (int)n; b <= 64; ++b) { starts[b] = acc; acc += counts[b]; }
+  for (int s = 0; s < num_decodes; ++s) {
+    const int np = ctx[s] > 0 ? (ctx[s] + 15) >> 4 : 0;
+    const int nfull = np / SP, rem = np - nfull * SP;
+    rem_at[s] = -1;
+    if (rem > 0) {
+      const int idx = starts[SP - rem]++;
+      rem_at[s] = idx;
+      if (idx < pl.dec_cap) dec[idx] = make_int4(s, nfull, ctx[s], qsl[s]);
+      n = std::max<int64_t>(n, idx + 1);
+    }
+  }
+  for (int64_t i = n; i < pl.dec_cap; ++i) dec[i] = make_int4(-1, 0, 0, 0);
+  int64_t nt = 0, ni = 0;
+  for (int s = num_decodes; s < num_seqs; ++s) {
+    const int Lq = qsl[s + 1] - qsl[s];
+    const int ntiles = Lq > 0 ? (Lq * G + PF_ROWS - 1) / PF_ROWS : 0;
+    for (int k = 0; k < ntiles; ++k) {
+      const int t = ntiles - 1 - k;
+      const int last_row = std::min(t * PF_ROWS + PF_ROWS, Lq * G) - 1;
+      const int kend = std::min(ctx[s], q_off[s] + last_row / G + 1);
+      const int ns = (kend + pl.pf_split_keys - 1) / pl.pf_split_keys;
+      if (nt < pl.pf_tile_cap) pft[nt] = make_int4(s, t, (int)ni, ns);
+      ++nt;
+      for (int ks = 0; ks < ns; ++ks, ++ni)
+        if (ni < pl.pf_item_cap) pfi[ni] = make_int4(s, t, ks, ns);
+    }
+  }
+  for (int64_t i = nt; i < pl.pf_tile_cap; ++i) pft[i] = make_int4(-1, 0, 0, 0);
+  for (int64_t i = ni; i < pl.pf_item_cap; ++i) pfi[i] = make_int4(-1, 0, 0, 0);
 }
 
 }  // namespace cb

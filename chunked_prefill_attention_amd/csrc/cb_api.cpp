@@ -117,6 +117,22 @@ int cb_attention_step(const void* q, const void* k_cache, const void* v_cache,
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                       int32_t num_pages, float scale, int32_t dtype, void* out,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  return cb::attention_step_impl(q, k_cache, v_cache, block_tables, block_table_stride, query_start_loc,
+                                 context_lens, q_offsets, num_seqs, num_decodes, num_tokens, max_context_len,
+                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale, dtype, out,
+                                 workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace cb {
+
+int attention_step_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        int32_t block_table_stride, const int32_t* query_start_loc, const int32_t* context_lens,
+                        const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes, int32_t num_tokens,
+                        int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t page_size, int32_t num_pages, float scale, int32_t dtype, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream, const WorkLists* lists) {
   cb::clear_error();
   if (int st = check_common(num_kv_heads, head_dim, page_size, num_pages, dtype)) return st;
   if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
@@ -177,7 +193,7 @@ int cb_attention_step(const void* q, const void* k_cache, const void* v_cache,
   if (!workspace || workspace_bytes < plan.bytes)
     return cb::fail(CB_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu%s)", plan.bytes, workspace_bytes,
                     workspace ? "" : ", null pointer");
-  return device_status(cb::launch_attention_bf16(a, plan, st), "cb_attention_step launch (bf16)");
+  return device_status(cb::launch_attention_bf16(a, plan, lists, st), "cb_attention_step launch (bf16)");
 }
 
-}  // extern "C"
+}  // namespace cb

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "cb_internal.h"
+#include "kernels.h"
 
 struct cb_engine {
   cb_engine_config cfg{};
@@ -20,6 +21,8 @@ struct cb_engine {
   int64_t slot_ints = 0;
   // device views of the pending step's metadata
   const int32_t *d_qsl = nullptr, *d_ctx = nullptr, *d_off = nullptr, *d_bt = nullptr, *d_slots = nullptr;
+  bool have_lists = false;  // bf16: the step's work lists were built on the host
+  cb::WorkLists lists{};
 };
 
 extern "C" {
@@ -97,7 +100,15 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   // worst case of this step's metadata, before the builder changes state
   const int64_t B = bc.max_requests_per_batch, T = bc.max_batch_tokens;
   const int64_t stride = (int64_t)cb::builder_max_pages_held(e->builder) + cb::ceil_div(T, CB_PAGE_SIZE) + 1;
-  const int64_t need = (B + 1) + 2 * B + B * std::min<int64_t>(stride, bc.num_pages) + T;
+  int64_t need = (B + 1) + 2 * B + B * std::min<int64_t>(stride, bc.num_pages) + T;
+  if (e->cfg.dtype == CB_BF16) {  // bound of the host-built work lists (int32 units)
+    const int64_t G = e->cfg.num_q_heads / e->cfg.num_kv_heads;
+    const int64_t pages = std::min<int64_t>(stride, bc.num_pages);
+    const int64_t dec_cap = B * cb::ceil_div(pages, 8);
+    const int64_t tiles = cb::ceil_div(T * G, 128) + B + 1;
+    const int64_t items = tiles * (cb::ceil_div(pages * CB_PAGE_SIZE, 512) + 1);
+    need += 4 * (dec_cap + tiles + items) + 2 * B + 32;
+  }
   if (need > e->slot_ints)
     return cb::fail(CB_ERR_CAPACITY, "step metadata may need %lld int32 per slot; the engine has %lld",
                     (long long)need, (long long)e->slot_ints);
@@ -122,6 +133,26 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   const size_t o_off = put(d.q_offsets, (size_t)d.num_seqs);
   const size_t o_bt = put(d.block_tables, (size_t)d.num_seqs * d.block_table_stride);
   const size_t o_sl = put(d.slot_mapping, (size_t)d.num_tokens);
+  e->have_lists = false;
+  if (e->cfg.dtype == CB_BF16 && d.num_tokens > 0) {
+    // the attention step's work lists, built here instead of by a device plan kernel
+    const cb::Bf16Plan pl = cb::plan_bf16(d.num_seqs, d.num_decodes, d.num_tokens, e->cfg.num_q_heads,
+                                          e->cfg.num_kv_heads, e->cfg.head_dim, std::max(d.max_context_len, 1));
+    const cb::WorkListLayout lay = cb::work_list_layout(pl, d.num_decodes);
+    const size_t at = (off + 3) & ~size_t(3);  // 16-byte aligned (int32 units)
+    if ((int64_t)(at + lay.bytes / 4) <= e->slot_ints) {
+      cb::build_work_lists(pl, d.num_seqs, d.num_decodes, e->cfg.num_q_heads / e->cfg.num_kv_heads,
+                           d.query_start_loc, d.context_lens, d.q_offsets, h + at);
+      const uint8_t* db = reinterpret_cast<const uint8_t*>(dv + at);
+      e->lists.dec_items = db + lay.dec_items;
+      e->lists.pf_items = db + lay.pf_items;
+      e->lists.pf_tiles = db + lay.pf_tiles;
+      e->lists.dec_first = reinterpret_cast<const int32_t*>(db + lay.dec_first);
+      e->lists.dec_rem = reinterpret_cast<const int32_t*>(db + lay.dec_rem);
+      e->have_lists = true;
+      off = at + lay.bytes / 4;
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(dv, h, off * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess ||
       hipEventRecord(e->copied[slot], s) != hipSuccess)
@@ -168,10 +199,11 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   int st = cb_kv_append(k_new, v_new, c.k_cache, c.v_cache, e->d_slots, d.num_tokens, c.num_kv_heads,
                         c.head_dim, c.builder.num_pages, CB_PAGE_SIZE, c.dtype, stream);
   if (st != CB_OK) return st;
-  st = cb_attention_step(q, c.k_cache, c.v_cache, e->d_bt, d.block_table_stride, e->d_qsl, e->d_ctx, e->d_off,
-                         d.num_seqs, d.num_decodes, d.num_tokens, d.max_context_len, c.num_q_heads,
-                         c.num_kv_heads, c.head_dim, CB_PAGE_SIZE, c.builder.num_pages, c.scale, c.dtype, out,
-                         c.workspace, c.workspace_bytes, stream);
+  st = cb::attention_step_impl(q, c.k_cache, c.v_cache, e->d_bt, d.block_table_stride, e->d_qsl, e->d_ctx,
+                               e->d_off, d.num_seqs, d.num_decodes, d.num_tokens, d.max_context_len,
+                               c.num_q_heads, c.num_kv_heads, c.head_dim, CB_PAGE_SIZE, c.builder.num_pages,
+                               c.scale, c.dtype, out, c.workspace, c.workspace_bytes, stream,
+                               e->have_lists ? &e->lists : nullptr);
   if (st == CB_OK) e->pending = false;
   return st;
 }

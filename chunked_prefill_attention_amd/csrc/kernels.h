@@ -48,10 +48,34 @@ struct Bf16Plan {
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
                    int32_t hkv, int32_t head_dim, int32_t max_context_len);
 
+// Work lists of one bf16 step built by the caller (the engine builds them on
+// the host and uploads them with the step's metadata); when given, the
+// device plan kernel is skipped.
+struct WorkLists {
+  const void* dec_items;     // int4 [dec_cap]: (sequence, split, context, query row); -1 = none
+  const void* pf_items;      // int4 [pf_item_cap]: (sequence, row tile, key split, splits)
+  const void* pf_tiles;      // int4 [pf_tile_cap]: (sequence, row tile, first item, splits)
+  const int32_t* dec_first;  // [num_decodes]
+  const int32_t* dec_rem;    // [num_decodes]
+};
+
+// Host layout of the work lists: byte offsets inside one buffer (16-byte aligned).
+struct WorkListLayout {
+  size_t dec_items, pf_items, pf_tiles, dec_first, dec_rem, bytes;
+};
+WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes);
+
+// Host version of the plan kernel (same lists, same order): fills `dst`
+// (laid out by work_list_layout) from the host copies of query_start_loc,
+// context_lens and q_offsets.
+void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t group,
+                      const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst);
+
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t head_dim,
                             int32_t num_pages, int32_t elem_bytes, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_attention_bf16(const AttnArgs& a, const Bf16Plan& plan, hipStream_t stream);
+hipError_t launch_attention_bf16(const AttnArgs& a, const Bf16Plan& plan, const WorkLists* lists,
+                                 hipStream_t stream);
 
 }  // namespace cb

@@ -153,8 +153,8 @@ size_t cb_attention_workspace_bytes(int32_t num_seqs, int32_t num_decodes, int32
  *                     ordered on one stream
  *
  * Values in cache slots at or past context_lens[s] (or NaN there) do not
- * affect the output.  Page ids >= num_pages are read as zero pages instead of
- * faulting.  Device-side preconditions that are not checked: the
+ * affect the output.  A page id >= num_pages (a broken precondition) is read
+ * as page 0 instead of faulting; the output is then unspecified.  Device-side preconditions that are not checked: the
  * query_start_loc / context_lens / q_offsets relations above and
  * context_lens <= max_context_len.
  * Errors: CB_ERR_INVALID (null pointers, negative or inconsistent sizes,
