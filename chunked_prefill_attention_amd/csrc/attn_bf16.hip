@@ -490,21 +490,15 @@ __device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const 
     const int r = rem / (D / 8), c16 = rem % (D / 8);
     const uint4 kv = stream_load(reinterpret_cast<const uint4*>(kb + r * D + c16 * 8));
     const int dr = rem >> 1, hf = rem & 1;
-    uint4 vv = stream_load(reinterpret_cast<const uint4*>(vb + dr * 16 + hf * 8));
-    const int n = ctx - (pg * 16 + hf * 8);  // valid tokens among these 8
-    if (n < 8) {
-      vv.x = keep16(vv.x, 0, n);
-      vv.y = keep16(vv.y, 2, n);
-      vv.z = keep16(vv.z, 4, n);
-      vv.w = keep16(vv.w, 6, n);
-    }
     st.k[i] = kv;
-    st.v[i] = vv;
+    st.v[i] = stream_load(reinterpret_cast<const uint4*>(vb + dr * 16 + hf * 8));
   }
 }
 
+// Stage tile kt in LDS; V tokens at or past the context end are zeroed here,
+// where the loaded data is consumed anyway.
 template <int D>
-__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, int tid) {
+__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, int kt, int ctx, int tid) {
   using Lds = PfLds<D>;
   uint8_t* kl = stage;
   uint8_t* vl = stage + Lds::K_BYTES;
@@ -516,8 +510,16 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
     *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = st.k[i];
     const int dr = rem >> 1, hf = rem & 1;
     uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(st.v[i].x, st.v[i].y);
-    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(st.v[i].z, st.v[i].w);
+    uint4 vv = st.v[i];
+    const int n = ctx - ((kt * 4 + pgl) * 16 + hf * 8);  // valid tokens among these 8
+    if (n < 8) {
+      vv.x = keep16(vv.x, 0, n);
+      vv.y = keep16(vv.y, 2, n);
+      vv.z = keep16(vv.z, 4, n);
+      vv.w = keep16(vv.w, 6, n);
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(vv.x, vv.y);
+    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(vv.z, vv.w);
   }
 }
 
@@ -568,8 +570,16 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     pids[i] = pg < npages ? btrow[pg] : -1;
   }
   __syncthreads();
-  PfStage<D> st;
-  if (kt0 < kt1) pf_fetch<D>(st, p, pids, kt0, kt0, ctx, kvh, tid);
+  // three-stage pipeline: tile kt+2 loads into registers while tile kt+1 sits
+  // in the second LDS stage and tile kt is computed.  Fetches past the last
+  // tile re-read it (clamped), so every iteration issues the same loads and
+  // the compiler never has to drain the one still in flight.
+  PfStage<D> sa, sb;
+  const int klast = kt1 - 1;
+  if (kt0 < kt1) {
+    pf_fetch<D>(sa, p, pids, kt0, kt0, ctx, kvh, tid);
+    pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), kt0, ctx, kvh, tid);
+  }
 
   bf16x8 qf[NK];
   {
@@ -586,13 +596,11 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   float m = -INFINITY, l = 0.f;
   const float c = p.scale_log2;
 
-  if (kt0 < kt1) pf_store<D>(st, smem, tid);
+  uint8_t* stage0 = smem;
+  uint8_t* stage1 = smem + Lds::STAGE;
+  if (kt0 < kt1) pf_store<D>(sa, stage0, kt0, ctx, tid);
   __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    uint8_t* cur = smem + ((kt - kt0) & 1) * Lds::STAGE;
-    uint8_t* nxt = smem + ((kt - kt0 + 1) & 1) * Lds::STAGE;
-    const bool more = kt + 1 < kt1;
-    if (more) pf_fetch<D>(st, p, pids, kt + 1, kt0, ctx, kvh, tid);
+  auto tile_step = [&](int kt, const uint8_t* cur) {
     const int kbase = kt * PF_KEYS;
     if (kbase < w_kend) {
       const uint8_t* kl = cur;
@@ -665,7 +673,16 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
           }
         }
     }
-    if (more) pf_store<D>(st, nxt, tid);
+  };
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    pf_fetch<D>(sa, p, pids, min(kt + 2, klast), kt0, ctx, kvh, tid);
+    tile_step(kt, stage0);
+    pf_store<D>(sb, stage1, min(kt + 1, klast), ctx, tid);  // tile kt+1 (clamped)
+    __syncthreads();
+    if (kt + 1 >= kt1) break;
+    pf_fetch<D>(sb, p, pids, min(kt + 3, klast), kt0, ctx, kvh, tid);
+    tile_step(kt + 1, stage1);
+    pf_store<D>(sa, stage0, min(kt + 2, klast), ctx, tid);  // tile kt+2 (clamped)
     __syncthreads();
   }
 
