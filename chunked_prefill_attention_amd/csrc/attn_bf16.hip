@@ -130,9 +130,36 @@ struct PfLds {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ short4v as_short4(uint2 v) { return __builtin_bit_cast(short4v, v); }
 
+// two floats -> one word of two bf16 (round to nearest even), one packed convert
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, b16x2));
+}
+
+// Reductions over lane pairs (l, l^32) and (l, l^16) through the cross-lane
+// swap instructions, without an LDS round trip.  Between them the two results
+// of a swap hold x[l] and x[l^k] at every lane, so max and sum of the pair are
+// the same on both lanes of a pair.
+__device__ __forceinline__ float pair_max32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float pair_max16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 // keep the first n (0..2*words) 16-bit elements of a little-endian word
@@ -356,8 +383,7 @@ __device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx,
     }
   }
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = pair_max32(pair_max16(mx));
   if ((mx - m) * c > CB_RESCALE_SLACK) {  // raise the running max (per head column)
     const float alpha = fast_exp2((m - mx) * c);  // m = -inf -> 0
     l *= alpha;
@@ -439,8 +465,7 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
     }
   }
 
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = pair_sum32(pair_sum16(l));
   if (hl >= G) return;
   if (nsplit == 1) {
     const float inv = 1.f / l;
@@ -631,7 +656,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair_max32(mx);
       const bool raise = (mx - m) * c > CB_RESCALE_SLACK;
       if (__builtin_amdgcn_ballot_w64(raise)) {
         const float alpha = raise ? fast_exp2((m - mx) * c) : 1.f;
@@ -686,7 +711,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     __syncthreads();
   }
 
-  l += __shfl_xor(l, 32);
+  l = pair_sum32(l);
   if (!rvalid) return;
   if (nsplit == 1) {
     const float inv = 1.f / l;
