@@ -1,4 +1,4 @@
-"""Plain-Python FIFO batch builder (test infrastructure only).
+"""Plain-Python batch builder (test infrastructure only).
 
 Follows these passages of the pages:
 
@@ -15,9 +15,19 @@ Follows these passages of the pages:
     cap (``max_requests_per_batch``).
   - "FIFO": active decodes first, then active prefills, then waiting
     requests in arrival order.
+  - "PrefillFirst": split prefills are carried to completion before decoding
+    resumes.
   - "Admission": a request that any allocator cannot hold is rejected and
     nothing is allocated; below ``safety_margin`` of free capacity new
     prefills are deferred and only active work continues.
+  - "Prefix caching": every full block gets a hash of its content; a later
+    request with the same prompt prefix reuses those blocks and skips their
+    prefill; shared blocks are reference counted and go back to the free pool
+    only when no request uses them any more.
+  - "Eviction" (of cached blocks): released blocks keep their content and
+    hash so that a later prefix can still match them; when uninitialised
+    blocks run out, the newest initialised ones lose their hash and are
+    handed out again.
 * Ultralytics glossary, "Chunked Prefill", "How chunked prefill works": one
   token per running decode first, then the remaining budget is filled with
   chunks of waiting prompts.
@@ -25,6 +35,10 @@ Follows these passages of the pages:
   scheduler looks like": finished sequences release their blocks at the top
   of the loop; waiting sequences are admitted from the head of the queue
   while blocks are free (strict head of line).
+* TNG blog on LLM serving performance, "Request-parallel prefill": prefills
+  of several requests may share a step, with a cap on how many of them have
+  a long prompt (the example: four prefills, at most one above 10,000
+  tokens), so that short prompts need not wait behind a long one.
 
 Readings where the pages are silent or ambiguous (also listed in the design doc):
 
@@ -45,24 +59,50 @@ Readings where the pages are silent or ambiguous (also listed in the design doc):
 * ``submit`` with ``tokens_cached > 0`` imports an in-flight request whose
   pages are allocated at once: an active prefill if ``tokens_cached <
   prompt_len``, else a decode that has produced ``tokens_cached - prompt_len
-  + 1`` tokens; imports and submissions share one arrival order.
+  + 1`` tokens; imports and submissions share one arrival order;
+* PrefillFirst picks active prefills, then active decodes, then waiting
+  requests; under every policy the step lists its decodes first;
+* the partial-prefill caps count the prefill chunks of one step (active and
+  newly admitted); a prefill over a cap is skipped (not stalled) and the
+  requests behind it are still considered; "long" means a prompt longer
+  than ``long_prefill_threshold`` tokens;
+* prefix sharing applies to requests submitted with their prompt tokens; a
+  block's identity is its tokens together with the identity of the block
+  before it, and only blocks wholly inside the prompt are hashed; a match
+  stops short of the last prompt token, which is always computed, so no
+  step writes into a shared page; blocks are registered when the step that
+  fills them is built, in order, and a request stops registering at its
+  first block whose identity is already registered; a reused block that no
+  request held counts against the free pages at admission; an allocation
+  takes a page that holds no registered block when there is one, else the
+  most recently released registered block, whose registration ends.
 
 Physical page ids are not unique (any free page is correct), so this model
-tracks page *counts* only.
+tracks page *counts* and block identities, not page ids.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass, field
+from typing import Optional
 
 import numpy as np
 
 WAITING, PREFILLING, DECODING, FINISHED = "waiting", "prefilling", "decoding", "finished"
+FIFO, PREFILL_FIRST = "fifo", "prefill_first"
 
 
 class SchedulerError(ValueError):
     def __init__(self, kind: str, msg: str):
         super().__init__(msg)
         self.kind = kind          # "invalid" or "capacity"
+
+
+@dataclass(eq=False)
+class Block:
+    """A registered full prompt block: the page that holds it is shared."""
+    serial: int                   # identity; never reused
+    key: tuple                    # (parent block's serial or -1, its tokens)
+    ref: int = 1                  # requests holding it
 
 
 @dataclass
@@ -73,8 +113,17 @@ class Request:
     arrival: int
     cached: int = 0
     generated: int = 0
-    pages: int = 0
     state: str = WAITING
+    tokens: Optional[tuple] = None
+    # one entry per held page: a Block when the page holds a registered block,
+    # else None (a page private to this request)
+    blocks: list = field(default_factory=list)
+    registered: int = 0           # leading blocks that are registered or matched
+    stop_registering: bool = False
+
+    @property
+    def pages(self) -> int:
+        return len(self.blocks)
 
 
 @dataclass
@@ -85,6 +134,8 @@ class ScheduledSeq:
     context_len: int       # KV length after this step's tokens
     is_decode: bool
     pages: int             # pages the request holds after this step's allocation
+    blocks: tuple = ()     # per held page: the block's serial, or -1 if private
+    prefix_hit: int = 0    # tokens reused from shared blocks at admission
 
 
 @dataclass
@@ -92,7 +143,7 @@ class Step:
     seqs: list = field(default_factory=list)
     finished: list = field(default_factory=list)   # released at the start of this step
     stalled: list = field(default_factory=list)
-    new_pages: int = 0
+    new_pages: int = 0     # pages taken from the free pool (fresh or reused blocks)
 
     @property
     def num_decodes(self) -> int:
@@ -107,13 +158,20 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-class FifoScheduler:
+class Scheduler:
     def __init__(self, max_batch_tokens: int, max_requests_per_batch: int, num_pages: int,
-                 page_size: int = 16, max_prefill_chunk: int = 0, safety_margin: float = 0.0):
+                 page_size: int = 16, max_prefill_chunk: int = 0, safety_margin: float = 0.0,
+                 policy: str = FIFO, max_partial_prefills: int = 0,
+                 max_long_partial_prefills: int = 0, long_prefill_threshold: int = 0,
+                 allow_block_sharing: bool = False):
         if max_batch_tokens < 1 or max_requests_per_batch < 1 or num_pages < 1 or page_size < 1:
             raise SchedulerError("invalid", "budgets and pool size must be positive")
         if max_prefill_chunk < 0 or not (0.0 <= safety_margin < 1.0):
             raise SchedulerError("invalid", "bad chunk cap or safety margin")
+        if policy not in (FIFO, PREFILL_FIRST):
+            raise SchedulerError("invalid", f"unknown policy {policy!r}")
+        if min(max_partial_prefills, max_long_partial_prefills, long_prefill_threshold) < 0:
+            raise SchedulerError("invalid", "prefill caps must be >= 0")
         self.max_batch_tokens = max_batch_tokens
         self.max_requests = max_requests_per_batch
         self.num_pages = num_pages
@@ -121,29 +179,95 @@ class FifoScheduler:
         self.chunk_cap = max_prefill_chunk
         # the margin is a float32 configuration value; compare in float64
         self.margin = float(np.float32(safety_margin))
-        self.free = num_pages
+        self.policy = policy
+        self.max_partial = max_partial_prefills
+        self.max_long = max_long_partial_prefills
+        self.long_threshold = long_prefill_threshold
+        self.sharing = bool(allow_block_sharing)
+        self.clean = num_pages            # free pages holding no registered block
+        self.cached: list[Block] = []     # released registered blocks, newest last
+        self.index: dict[tuple, Block] = {}
+        self._serials = 0
         self.requests: dict[int, Request] = {}
         self._arrivals = 0
         self.total_stalls = 0
+        self.prefix_hit_tokens = 0
+
+    # -- the page pool ------------------------------------------------------------
+    @property
+    def free(self) -> int:
+        return self.clean + len(self.cached)
+
+    def _take(self):
+        """One page for private use: a clean page if any, else the newest cached block."""
+        assert self.free > 0
+        if self.clean > 0:
+            self.clean -= 1
+        else:
+            blk = self.cached.pop()
+            if self.index.get(blk.key) is blk:
+                del self.index[blk.key]
+        return None
+
+    def _release(self, entry):
+        if entry is None:
+            self.clean += 1
+            return
+        entry.ref -= 1
+        if entry.ref == 0:
+            self.cached.append(entry)
+
+    def _key(self, parent, tokens, i):
+        return (parent.serial if parent is not None else -1,
+                tuple(tokens[i * self.page:(i + 1) * self.page]))
+
+    def _match(self, r):
+        """Registered blocks matching r's prompt, leaving its last token to compute."""
+        found, parent = [], None
+        for i in range((r.prompt_len - 1) // self.page):
+            blk = self.index.get(self._key(parent, r.tokens, i))
+            if blk is None:
+                break
+            found.append(blk)
+            parent = blk
+        return found
+
+    def _register(self, r):
+        full = min(r.cached, r.prompt_len) // self.page
+        while r.registered < full and not r.stop_registering:
+            i = r.registered
+            parent = r.blocks[i - 1] if i > 0 else None
+            key = self._key(parent, r.tokens, i)
+            if key in self.index:
+                r.stop_registering = True
+                break
+            blk = Block(self._serials, key)
+            self._serials += 1
+            self.index[key] = blk
+            r.blocks[i] = blk
+            r.registered += 1
 
     # -- submission ---------------------------------------------------------------
-    def submit(self, req_id: int, prompt_len: int, output_len: int, tokens_cached: int = 0):
+    def submit(self, req_id: int, prompt_len: int, output_len: int, tokens_cached: int = 0,
+               tokens=None):
         if req_id in self.requests:
             raise SchedulerError("invalid", f"duplicate request id {req_id}")
         if prompt_len < 1 or output_len < 1 or tokens_cached < 0:
             raise SchedulerError("invalid", "lengths must be positive")
+        if tokens is not None and (len(tokens) != prompt_len or tokens_cached > 0):
+            raise SchedulerError("invalid", "tokens must hold the whole prompt of a new request")
         final_kv = prompt_len + output_len - 1
         if tokens_cached >= final_kv and tokens_cached > 0:
             raise SchedulerError("invalid", "request has nothing left to do")
         if _ceil_div(final_kv, self.page) > self.num_pages:
             raise SchedulerError("capacity", "request can never fit the page pool")
-        r = Request(req_id, prompt_len, output_len, self._arrivals)
+        r = Request(req_id, prompt_len, output_len, self._arrivals,
+                    tokens=tuple(int(t) for t in tokens) if tokens is not None else None)
         if tokens_cached > 0:
             need = _ceil_div(tokens_cached, self.page)
             if need > self.free:
                 raise SchedulerError("capacity", "not enough free pages to import")
-            self.free -= need
-            r.pages = need
+            r.blocks = [self._take() for _ in range(need)]
             r.cached = tokens_cached
             if tokens_cached < prompt_len:
                 r.state = PREFILLING
@@ -158,75 +282,116 @@ class FifoScheduler:
         return sorted((r for r in self.requests.values() if r.state == state),
                       key=lambda r: r.arrival)
 
+    def _is_long(self, r) -> bool:
+        return r.prompt_len > self.long_threshold
+
     def step(self) -> Step:
         st = Step()
         # release what finished last step
         for r in self._ordered(FINISHED):
-            self.free += r.pages
+            for entry in r.blocks:
+                self._release(entry)
             st.finished.append(r.req_id)
             del self.requests[r.req_id]
 
-        tokens_left = self.max_batch_tokens
-        slots_left = self.max_requests
-        scheduled = []        # (request, q_len, is_decode)
+        budget = {"tokens": self.max_batch_tokens, "slots": self.max_requests,
+                  "prefills": 0, "long": 0}
+        scheduled = []        # (request, q_len, is_decode, prefix_hit)
 
-        # 1. active decodes, one token each
-        for r in self._ordered(DECODING):
-            if tokens_left < 1 or slots_left < 1:
-                break
-            need = 1 if r.cached % self.page == 0 else 0
-            if need > self.free:
-                st.stalled.append(r.req_id)
-                continue
-            self.free -= need
-            r.pages += need
-            st.new_pages += need
-            scheduled.append((r, 1, True))
-            tokens_left -= 1
-            slots_left -= 1
+        def room() -> bool:
+            return budget["tokens"] >= 1 and budget["slots"] >= 1
 
-        # 2. active prefills, each taking every token that still fits
-        for r in self._ordered(PREFILLING):
-            if tokens_left < 1 or slots_left < 1:
-                break
-            chunk = min(r.prompt_len - r.cached, tokens_left)
-            if self.chunk_cap > 0:
-                chunk = min(chunk, self.chunk_cap)
-            chunk = min(chunk, (r.pages + self.free) * self.page - r.cached)
-            if chunk <= 0:
-                st.stalled.append(r.req_id)
-                continue
-            need = _ceil_div(r.cached + chunk, self.page) - r.pages
-            self.free -= need
-            r.pages += need
-            st.new_pages += need
-            scheduled.append((r, chunk, False))
-            tokens_left -= chunk
-            slots_left -= 1
+        def prefill_capped(r) -> bool:
+            if self.max_partial > 0 and budget["prefills"] >= self.max_partial:
+                return True
+            return self.max_long > 0 and self._is_long(r) and budget["long"] >= self.max_long
 
-        # 3. waiting requests in arrival order, strict head of line
-        for r in self._ordered(WAITING):
-            if tokens_left < 1 or slots_left < 1:
-                break
-            chunk = min(r.prompt_len, tokens_left)
-            if self.chunk_cap > 0:
-                chunk = min(chunk, self.chunk_cap)
-            need = _ceil_div(chunk, self.page)
-            if need > self.free:
-                break
-            if self.margin > 0.0 and (self.free - need) < self.margin * self.num_pages:
-                break
-            self.free -= need
-            r.pages = need
-            r.state = PREFILLING
-            st.new_pages += need
-            scheduled.append((r, chunk, False))
-            tokens_left -= chunk
-            slots_left -= 1
+        def take_prefill(r, n):
+            budget["tokens"] -= n
+            budget["slots"] -= 1
+            budget["prefills"] += 1
+            budget["long"] += 1 if self._is_long(r) else 0
 
-        # emit in scheduling order and advance each request
-        for r, n, is_decode in scheduled:
-            st.seqs.append(ScheduledSeq(r.req_id, n, r.cached, r.cached + n, is_decode, r.pages))
+        # active decodes, one token each
+        def decodes():
+            for r in self._ordered(DECODING):
+                if not room():
+                    break
+                need = 1 if r.cached % self.page == 0 else 0
+                if need > self.free:
+                    st.stalled.append(r.req_id)
+                    continue
+                for _ in range(need):
+                    r.blocks.append(self._take())
+                st.new_pages += need
+                scheduled.append((r, 1, True, 0))
+                budget["tokens"] -= 1
+                budget["slots"] -= 1
+
+        # active prefills, each taking every token that still fits
+        def active_prefills():
+            for r in self._ordered(PREFILLING):
+                if not room():
+                    break
+                if prefill_capped(r):
+                    continue
+                chunk = min(r.prompt_len - r.cached, budget["tokens"])
+                if self.chunk_cap > 0:
+                    chunk = min(chunk, self.chunk_cap)
+                chunk = min(chunk, (r.pages + self.free) * self.page - r.cached)
+                if chunk <= 0:
+                    st.stalled.append(r.req_id)
+                    continue
+                need = _ceil_div(r.cached + chunk, self.page) - r.pages
+                for _ in range(need):
+                    r.blocks.append(self._take())
+                st.new_pages += need
+                scheduled.append((r, chunk, False, 0))
+                take_prefill(r, chunk)
+
+        # waiting requests in arrival order, strict head of line on pages
+        def waiting():
+            for r in self._ordered(WAITING):
+                if not room():
+                    break
+                if prefill_capped(r):
+                    continue
+                matched = self._match(r) if (self.sharing and r.tokens is not None) else []
+                start = len(matched) * self.page
+                chunk = min(r.prompt_len - start, budget["tokens"])
+                if self.chunk_cap > 0:
+                    chunk = min(chunk, self.chunk_cap)
+                fresh = _ceil_div(chunk, self.page)
+                reused = sum(1 for b in matched if b.ref == 0)
+                need = fresh + reused
+                if need > self.free:
+                    break
+                if self.margin > 0.0 and (self.free - need) < self.margin * self.num_pages:
+                    break
+                for b in matched:
+                    if b.ref == 0:
+                        self.cached.remove(b)
+                    b.ref += 1
+                r.blocks = list(matched) + [self._take() for _ in range(fresh)]
+                r.cached = start
+                r.registered = len(matched)
+                r.state = PREFILLING
+                st.new_pages += need
+                self.prefix_hit_tokens += start
+                scheduled.append((r, chunk, False, start))
+                take_prefill(r, chunk)
+
+        if self.policy == FIFO:
+            decodes()
+            active_prefills()
+        else:
+            active_prefills()
+            decodes()
+        waiting()
+
+        # emit decodes first, each class in scheduling order, and advance
+        ordered = [x for x in scheduled if x[2]] + [x for x in scheduled if not x[2]]
+        for r, n, is_decode, hit in ordered:
             r.cached += n
             if is_decode:
                 r.generated += 1
@@ -234,6 +399,11 @@ class FifoScheduler:
                 r.generated = 1
             if r.generated >= 1:
                 r.state = FINISHED if r.generated >= r.output_len else DECODING
+            if self.sharing and r.tokens is not None:
+                self._register(r)
+            st.seqs.append(ScheduledSeq(
+                r.req_id, n, r.cached - n, r.cached, is_decode, r.pages,
+                tuple(b.serial if b is not None else -1 for b in r.blocks), hit))
         self.total_stalls += len(st.stalled)
         return st
 
@@ -246,3 +416,7 @@ class FifoScheduler:
 
     def idle(self) -> bool:
         return not self.requests
+
+
+# the pages' default scheduler
+FifoScheduler = Scheduler

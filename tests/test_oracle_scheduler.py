@@ -145,3 +145,204 @@ def test_submit_errors():
     assert e.value.kind == "capacity"
     with pytest.raises(SchedulerError):
         s.submit(3, 0, 1)
+
+
+# --- scheduler variants ------------------------------------------------------
+def test_prefill_first_serves_active_prefills_before_decodes():
+    """PrefillFirst: the split prefill takes the budget first; decodes get the rest."""
+    def build(policy, budget):
+        s = FifoScheduler(budget, 128, 100, policy=policy)
+        s.submit(0, 20, 5, tokens_cached=4)          # active prefill, 16 tokens left
+        for i in (1, 2, 3):
+            s.submit(i, 8, 5, tokens_cached=10)      # decodes
+        return s.step()
+    fifo = build("fifo", 10)
+    assert [(x.req_id, x.q_len) for x in fifo.seqs] == [(1, 1), (2, 1), (3, 1), (0, 7)]
+    pf = build("prefill_first", 10)
+    assert [(x.req_id, x.q_len) for x in pf.seqs] == [(0, 10)]
+    pf = build("prefill_first", 18)                  # 16 for the prefill, 2 decodes
+    assert [(x.req_id, x.q_len) for x in pf.seqs] == [(1, 1), (2, 1), (0, 16)]
+    assert pf.num_decodes == 2                       # decodes are listed first
+
+
+def test_partial_prefill_caps_four_prefills_one_long():
+    """The page's example: up to four prefills per step, at most one over 10,000 tokens."""
+    s = FifoScheduler(2048, 128, 10000, max_prefill_chunk=512, max_partial_prefills=4,
+                      max_long_partial_prefills=1, long_prefill_threshold=10000)
+    s.submit(0, 20000, 2)     # long
+    s.submit(1, 15000, 2)     # long: must wait for 0's prefill
+    s.submit(2, 500, 2)       # short: fast lane past request 1
+    s.submit(3, 300, 2)
+    s.submit(4, 200, 2)
+    s.submit(5, 100, 2)       # fifth prefill: over the cap of four
+    st = s.step()
+    assert [(x.req_id, x.q_offset, x.q_len) for x in st.seqs] == [
+        (0, 0, 512), (2, 0, 500), (3, 0, 300), (4, 0, 200)]
+    st = s.step()
+    # 2, 3, 4 decode; 0 continues; 1 stays behind the long cap; 5 fits now
+    assert [(x.req_id, x.q_len) for x in st.seqs] == [(2, 1), (3, 1), (4, 1), (0, 512), (5, 100)]
+    # with one prefill per step, prefills run one request at a time
+    s = FifoScheduler(2048, 128, 10000, max_prefill_chunk=512, max_partial_prefills=1)
+    s.submit(0, 700, 2)
+    s.submit(1, 10, 2)
+    assert [(x.req_id, x.q_len) for x in s.step().seqs] == [(0, 512)]
+    assert [(x.req_id, x.q_len) for x in s.step().seqs] == [(0, 188)]
+    assert [(x.req_id, x.q_len) for x in s.step().seqs] == [(0, 1), (1, 10)]
+
+
+# --- prefix sharing -------------------------------------------------------------
+def _prompt(n, seed=0, vocab=1000):
+    return [int(t) for t in np.random.default_rng(seed).integers(0, vocab, n)]
+
+
+def _sharing(pages=100, budget=256, **kw):
+    return FifoScheduler(budget, 128, pages, allow_block_sharing=True, **kw)
+
+
+def test_shared_prefix_skips_matched_blocks():
+    s = _sharing()
+    p = _prompt(40)
+    s.submit(0, 40, 4, tokens=p)
+    a = s.step().seqs[0]
+    assert (a.q_offset, a.q_len, a.prefix_hit) == (0, 40, 0)
+    assert a.blocks[2] == -1 and a.blocks[0] >= 0 and a.blocks[1] >= 0   # 2 full blocks registered
+    s.submit(1, 40, 4, tokens=p)
+    st = s.step()
+    b = [x for x in st.seqs if x.req_id == 1][0]
+    # blocks 0 and 1 (32 tokens) are reused; the last 8 prompt tokens are computed
+    assert (b.q_offset, b.q_len, b.context_len, b.prefix_hit) == (32, 8, 40, 32)
+    assert b.blocks[:2] == a.blocks[:2] and b.blocks[2] == -1
+    # 3 pages for request 0, 1 more for its decode at 40 -> no; 40 % 16 != 0, so 3,
+    # plus 1 private page for request 1
+    assert s.pages_in_use() == 4 and s.prefix_hit_tokens == 32
+
+
+def test_last_prompt_token_is_always_computed():
+    s = _sharing()
+    p = _prompt(32, seed=1)
+    s.submit(0, 32, 3, tokens=p)
+    s.step()
+    s.submit(1, 32, 3, tokens=p)
+    b = [x for x in s.step().seqs if x.req_id == 1][0]
+    # two full blocks are registered, but only one can be reused: the second
+    # holds the last prompt token, which must be computed
+    assert (b.q_offset, b.q_len, b.prefix_hit) == (16, 16, 16)
+    assert b.blocks[1] == -1
+
+
+def test_partial_match_and_no_match():
+    s = _sharing()
+    p = _prompt(64, seed=2)
+    s.submit(0, 64, 2, tokens=p)
+    s.step()
+    q = list(p)
+    q[20] += 1                              # differs inside block 1
+    s.submit(1, 64, 2, tokens=q)
+    r = list(p)
+    r[0] += 1                               # differs in block 0
+    s.submit(2, 64, 2, tokens=r)
+    st = s.step()
+    hits = {x.req_id: (x.q_offset, x.prefix_hit) for x in st.seqs if not x.is_decode}
+    assert hits == {1: (16, 16), 2: (0, 0)}
+
+
+def test_shared_blocks_are_reference_counted_and_reusable_after_release():
+    s = _sharing(pages=20)
+    p = _prompt(48, seed=3)
+    s.submit(0, 48, 2, tokens=p)            # prefill step, then one decode step
+    s.step()
+    s.submit(1, 48, 2, tokens=p)
+    s.step()                                # 0 decodes (finishes); 1 reuses 2 blocks
+    held = s.pages_in_use()
+    st = s.step()                           # 0 released; its shared blocks stay held by 1
+    assert st.finished == [0]
+    # 0's block 2 (registered, now unheld) and its decode page are free; 1's
+    # decode at 48 takes a fresh page
+    assert s.pages_in_use() == held - 2 + 1
+    s.step()                                # 1 (finished last step) released
+    assert s.pages_in_use() == 0 and s.free == 20
+    assert len(s.cached) == 3               # blocks 0, 1, 2 keep their registration
+    s.submit(2, 48, 2, tokens=p)
+    b = s.step().seqs[0]
+    assert (b.q_offset, b.prefix_hit) == (32, 32)   # released blocks still match
+    assert s.pages_in_use() == 3
+
+
+def test_newest_cached_block_is_demoted_first():
+    s = _sharing(pages=6, budget=128)
+    p, q = _prompt(33, seed=4), _prompt(33, seed=5)
+    s.submit(0, 33, 1, tokens=p)            # output 1: finishes with its prefill
+    s.submit(1, 33, 1, tokens=q)
+    s.step()
+    s.step()                                # both released: 0's then 1's pages
+    assert s.free == 6 and s.clean == 2 and len(s.cached) == 4
+    s.submit(2, 40, 1, tokens=_prompt(40, seed=6))   # 3 pages: 2 clean + 1 demoted
+    s.step()
+    # the newest cached block (1's block 1) lost its registration
+    s.step()
+    s.submit(3, 33, 1, tokens=q)
+    s.submit(4, 33, 1, tokens=p)
+    st = s.step()
+    hits = {x.req_id: x.prefix_hit for x in st.seqs}
+    assert hits == {3: 16, 4: 32}
+
+
+def test_identical_prompts_admitted_together_do_not_share():
+    s = _sharing()
+    p = _prompt(40, seed=7)
+    s.submit(0, 40, 3, tokens=p)
+    s.submit(1, 40, 3, tokens=p)
+    st = s.step()
+    a, b = st.seqs
+    assert a.prefix_hit == b.prefix_hit == 0
+    assert a.blocks[:2] != b.blocks[:2] and b.blocks == (-1, -1, -1)   # 1 stops registering
+    s.submit(2, 40, 3, tokens=p)
+    c = [x for x in s.step().seqs if x.req_id == 2][0]
+    assert c.blocks[:2] == a.blocks[:2] and c.prefix_hit == 32
+
+
+def test_sharing_off_or_without_tokens_changes_nothing():
+    p = _prompt(40, seed=8)
+    for kw in ({"allow_block_sharing": False}, {"allow_block_sharing": True}):
+        s = FifoScheduler(256, 128, 100, **kw)
+        s.submit(0, 40, 3, tokens=p)
+        s.step()
+        s.submit(1, 40, 3, tokens=p if not kw["allow_block_sharing"] else None)
+        b = [x for x in s.step().seqs if x.req_id == 1][0]
+        assert (b.q_offset, b.prefix_hit) == (0, 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sharing_pool_invariants_on_random_traces(seed):
+    """Pages are conserved and every block's count equals the requests holding it."""
+    rng = np.random.default_rng(100 + seed)
+    base = [_prompt(int(rng.integers(16, 120)), seed=1000 * seed + k, vocab=50) for k in range(4)]
+    s = FifoScheduler(96, 16, 60, max_prefill_chunk=int(rng.integers(0, 3)) * 24,
+                      allow_block_sharing=True)
+    rid = 0
+    for _ in range(300):
+        if rng.random() < 0.5:
+            b = base[int(rng.integers(0, 4))]
+            n = int(rng.integers(1, len(b) + 1))
+            toks = list(b[:n]) + _prompt(int(rng.integers(0, 20)), seed=rid, vocab=50)
+            try:
+                s.submit(rid, len(toks), int(rng.integers(1, 12)), tokens=toks)
+            except Exception:
+                pass
+            rid += 1
+        s.step()
+        held = {}
+        private = 0
+        for r in s.requests.values():
+            for e in r.blocks:
+                if e is None:
+                    private += 1
+                else:
+                    held[id(e)] = held.get(id(e), 0) + 1
+                    assert e.ref >= 1
+        objs = {id(e): e for r in s.requests.values() for e in r.blocks if e is not None}
+        assert all(objs[k].ref == v for k, v in held.items())
+        assert all(c.ref == 0 and id(c) not in held for c in s.cached)
+        assert s.pages_in_use() == private + len(held)
+        assert 0 <= s.clean and s.free <= s.num_pages
+    assert s.prefix_hit_tokens > 0
