@@ -18,9 +18,9 @@ from dataclasses import dataclass
 import numpy as np
 
 from ._lib import (BuilderConfig, BuilderStats, CbError, StepDesc, check, load,
-                   CB_F32, CB_BF16, PAGE_SIZE, LIB_PATH)
+                   CB_F32, CB_BF16, CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST, PAGE_SIZE, LIB_PATH)
 
-__all__ = ["kv_append", "attention_step", "attention_workspace_bytes", "Builder", "Step",
+__all__ = ["kv_append", "attention_step", "attention_workspace_bytes", "Builder", "Step", "builder_config",
            "CbError", "CB_F32", "CB_BF16", "PAGE_SIZE", "LIB_PATH", "load"]
 
 
@@ -138,6 +138,7 @@ class Step:
     slot_mapping: np.ndarray
     finished_ids: np.ndarray
     stalled_ids: np.ndarray
+    prefix_hit_tokens: int = 0
 
     @property
     def q_lens(self) -> np.ndarray:
@@ -150,18 +151,35 @@ def _arr(ptr, n, dtype):
     return np.ctypeslib.as_array(ptr, shape=(n,)).copy().astype(dtype, copy=False)
 
 
+POLICIES = {"fifo": CB_POLICY_FIFO, "prefill_first": CB_POLICY_PREFILL_FIRST}
+
+
+def builder_config(max_batch_tokens, max_requests_per_batch, num_pages, max_prefill_chunk=0,
+                   safety_margin=0.0, page_shuffle_seed=0, policy="fifo", max_partial_prefills=0,
+                   max_long_partial_prefills=0, long_prefill_threshold=0,
+                   allow_block_sharing=False) -> BuilderConfig:
+    """The builder's C configuration; argument meanings as in include/cb.h."""
+    if policy not in POLICIES:
+        raise ValueError(f"policy must be one of {sorted(POLICIES)}")
+    return BuilderConfig(max_batch_tokens, max_requests_per_batch, num_pages, PAGE_SIZE,
+                         max_prefill_chunk, safety_margin, page_shuffle_seed, POLICIES[policy],
+                         max_partial_prefills, max_long_partial_prefills, long_prefill_threshold,
+                         1 if allow_block_sharing else 0)
+
+
 class Builder:
-    """FIFO batch builder (C++): token budget, request cap, page budget, safety margin."""
+    """Batch builder (C++): token budget, request cap, page budget, safety margin,
+    FIFO or PrefillFirst policy, partial-prefill caps, prefix block sharing."""
 
     def __init__(self, max_batch_tokens, max_requests_per_batch, num_pages, max_prefill_chunk=0,
-                 safety_margin=0.0, page_shuffle_seed=0, _handle=None, _owned=True):
+                 safety_margin=0.0, page_shuffle_seed=0, _handle=None, _owned=True, **policy_kw):
         self._lib = load()
         self._owned = _owned
         if _handle is not None:
             self._h = C.c_void_p(_handle) if isinstance(_handle, int) else _handle
             return
-        cfg = BuilderConfig(max_batch_tokens, max_requests_per_batch, num_pages, PAGE_SIZE,
-                            max_prefill_chunk, safety_margin, page_shuffle_seed)
+        cfg = builder_config(max_batch_tokens, max_requests_per_batch, num_pages, max_prefill_chunk,
+                             safety_margin, page_shuffle_seed, **policy_kw)
         h = C.c_void_p()
         check(self._lib.cb_builder_create(C.byref(cfg), C.byref(h)))
         self._h = h
@@ -179,8 +197,19 @@ class Builder:
 
     __del__ = close
 
-    def submit(self, req_id: int, prompt_len: int, output_len: int, tokens_cached: int = 0) -> None:
-        check(self._lib.cb_builder_submit(self._h, req_id, prompt_len, output_len, tokens_cached))
+    def submit(self, req_id: int, prompt_len: int, output_len: int, tokens_cached: int = 0,
+               tokens=None) -> None:
+        """Queue a request; with ``tokens`` (the whole prompt) it may share prefix blocks."""
+        if tokens is None:
+            check(self._lib.cb_builder_submit(self._h, req_id, prompt_len, output_len, tokens_cached))
+            return
+        if tokens_cached:
+            raise ValueError("tokens are given for new requests only")
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        if t.shape != (prompt_len,):
+            raise ValueError("tokens must hold prompt_len ids")
+        check(self._lib.cb_builder_submit_tokens(self._h, req_id, t.ctypes.data_as(C.POINTER(C.c_int32)),
+                                                 prompt_len, output_len))
 
     def step(self) -> Step:
         d = StepDesc()
@@ -191,7 +220,7 @@ class Builder:
                     _arr(d.context_lens, n, np.int32), _arr(d.q_offsets, n, np.int32),
                     _arr(d.block_tables, n * st, np.int32).reshape(n, st),
                     _arr(d.slot_mapping, T, np.int32), _arr(d.finished_ids, d.num_finished, np.int64),
-                    _arr(d.stalled_ids, d.num_stalled, np.int64))
+                    _arr(d.stalled_ids, d.num_stalled, np.int64), d.prefix_hit_tokens)
 
     def block_table(self, req_id: int) -> np.ndarray:
         n = C.c_int32()

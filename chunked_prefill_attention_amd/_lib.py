@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libcb.so")
 
 CB_OK, CB_ERR_INVALID, CB_ERR_UNSUPPORTED, CB_ERR_WORKSPACE, CB_ERR_DEVICE, CB_ERR_CAPACITY = 0, -1, -2, -3, -4, -5
 CB_F32, CB_BF16 = 0, 1
+CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST = 0, 1
 PAGE_SIZE = 16
 
 i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
@@ -23,13 +24,15 @@ P_i64 = C.POINTER(C.c_int64)
 class BuilderConfig(C.Structure):
     _fields_ = [("max_batch_tokens", i32), ("max_requests_per_batch", i32), ("num_pages", i32),
                 ("page_size", i32), ("max_prefill_chunk", i32), ("safety_margin", f32),
-                ("page_shuffle_seed", C.c_uint64)]
+                ("page_shuffle_seed", C.c_uint64), ("policy", i32), ("max_partial_prefills", i32),
+                ("max_long_partial_prefills", i32), ("long_prefill_threshold", i32),
+                ("allow_block_sharing", i32)]
 
 
 class StepDesc(C.Structure):
     _fields_ = [("num_seqs", i32), ("num_decodes", i32), ("num_tokens", i32), ("max_query_len", i32),
                 ("max_context_len", i32), ("block_table_stride", i32), ("num_finished", i32),
-                ("num_stalled", i32), ("new_pages", i32),
+                ("num_stalled", i32), ("new_pages", i32), ("prefix_hit_tokens", i32),
                 ("req_ids", P_i64), ("query_start_loc", P_i32), ("context_lens", P_i32),
                 ("q_offsets", P_i32), ("block_tables", P_i32), ("slot_mapping", P_i32),
                 ("finished_ids", P_i64), ("stalled_ids", P_i64)]
@@ -39,7 +42,8 @@ class BuilderStats(C.Structure):
     _fields_ = [("num_pages", i32), ("free_pages", i32), ("num_waiting", i32), ("num_prefilling", i32),
                 ("num_decoding", i32), ("num_finished_pending", i32), ("used_slots", i64),
                 ("allocated_slots", i64), ("steps", i64), ("total_stalls", i64),
-                ("total_finished", i64), ("fragmentation", C.c_double)]
+                ("total_finished", i64), ("fragmentation", C.c_double), ("prefix_hit_tokens", i64),
+                ("cached_pages", i32)]
 
 
 class EngineConfig(C.Structure):
@@ -62,6 +66,7 @@ SIGNATURES = {
     "cb_builder_clone": (C.c_int, [vp, C.POINTER(vp)]),
     "cb_builder_destroy": (None, [vp]),
     "cb_builder_submit": (C.c_int, [vp, i64, i32, i32, i32]),
+    "cb_builder_submit_tokens": (C.c_int, [vp, i64, P_i32, i32, i32]),
     "cb_builder_step": (C.c_int, [vp, C.POINTER(StepDesc)]),
     "cb_builder_block_table": (C.c_int, [vp, i64, P_i32, i32, P_i32]),
     "cb_builder_stats_get": (C.c_int, [vp, C.POINTER(BuilderStats)]),

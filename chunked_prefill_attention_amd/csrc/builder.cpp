@@ -8,9 +8,18 @@
 // looks like": release finished requests, admit from the head of the waiting
 // queue while blocks are free, then batch decode tokens and prefill chunks.
 //
+// transformers, "PrefillFirst": split prefills finish before decoding resumes.
+// TNG blog, "Request-parallel prefill": a cap on prefills per step and on the
+// long ones among them.  transformers, "Prefix caching": full blocks carry a
+// content identity, later requests with the same prefix reuse them, shared
+// blocks are reference counted; released ones stay matchable until their page
+// is needed again (newest released first).
+//
 // Per step the builder walks its live requests once (O(requests + new pages))
 // and writes the ragged descriptor into arrays it owns, ready to be copied to
-// the device in one go.  Pages come from a LIFO free list of physical ids.
+// the device in one go.  Pages come from a LIFO stack of physical ids that
+// hold no registered block; with sharing on, released registered blocks wait
+// in a newest-last list and are taken only when that stack is empty.
 #include <algorithm>
 #include <cstring>
 #include <memory>
@@ -32,7 +41,10 @@ struct Request {
   int32_t cached = 0;     // tokens whose K/V is in the cache
   int32_t generated = 0;  // output tokens produced so far
   State state = State::Waiting;
-  std::vector<int32_t> pages;  // block table, logical order
+  std::vector<int32_t> pages;   // block table, logical order
+  std::vector<int32_t> tokens;  // prompt tokens (empty: no sharing)
+  int32_t registered = 0;       // leading blocks registered or matched
+  bool stop_registering = false;
 };
 
 uint64_t splitmix64(uint64_t& x) {
@@ -42,28 +54,160 @@ uint64_t splitmix64(uint64_t& x) {
   return z ^ (z >> 31);
 }
 
+// Identity of a full prompt block: its tokens and the page (with that page's
+// generation) holding the block before it.  Every hand-out of a page bumps its
+// generation, so keys made under an earlier use of the parent page go stale.
+struct BlockKey {
+  int32_t parent = -1;
+  uint32_t parent_gen = 0;
+  int32_t tok[CB_PAGE_SIZE] = {};
+  bool operator==(const BlockKey& o) const {
+    return parent == o.parent && parent_gen == o.parent_gen && std::memcmp(tok, o.tok, sizeof tok) == 0;
+  }
+};
+
+struct BlockKeyHash {
+  size_t operator()(const BlockKey& k) const {
+    uint64_t h = ((uint64_t)(uint32_t)k.parent << 32) ^ k.parent_gen;
+    uint64_t x = h;
+    for (int i = 0; i < CB_PAGE_SIZE; ++i) {
+      x ^= (uint64_t)(uint32_t)k.tok[i] + 0x9E3779B97F4A7C15ull * (uint64_t)(i + 1);
+      h ^= splitmix64(x);
+    }
+    return (size_t)h;
+  }
+};
+
+// The physical page pool.
+struct PagePool {
+  std::vector<int32_t> clean;  // stack of pages holding no registered block; back() goes next
+  bool sharing = false;
+  // per page, sized only with sharing on
+  std::vector<int32_t> ref;
+  std::vector<uint32_t> gen;
+  std::vector<uint8_t> hashed;
+  std::vector<BlockKey> key;
+  std::vector<int32_t> prev, next;  // list of released registered blocks, newest at tail
+  int32_t head = -1, tail = -1, cached = 0;
+  std::unordered_map<BlockKey, int32_t, BlockKeyHash> index;
+
+  int32_t free() const { return (int32_t)clean.size() + cached; }
+
+  void unlink(int32_t p) {
+    (prev[p] >= 0 ? next[prev[p]] : head) = next[p];
+    (next[p] >= 0 ? prev[next[p]] : tail) = prev[p];
+    prev[p] = next[p] = -1;
+    cached--;
+  }
+  void push_cached(int32_t p) {
+    prev[p] = tail;
+    next[p] = -1;
+    (tail >= 0 ? next[tail] : head) = p;
+    tail = p;
+    cached++;
+  }
+  // One page for private use: a clean page if any, else the newest released
+  // registered block, which loses its registration.
+  int32_t take() {
+    int32_t p;
+    if (!clean.empty()) {
+      p = clean.back();
+      clean.pop_back();
+    } else {
+      p = tail;
+      unlink(p);
+      auto it = index.find(key[p]);
+      if (it != index.end() && it->second == p) index.erase(it);
+      hashed[p] = 0;
+    }
+    if (sharing) {
+      gen[p]++;
+      ref[p] = 1;
+    }
+    return p;
+  }
+  void release(int32_t p) {
+    if (!sharing) {
+      clean.push_back(p);
+      return;
+    }
+    if (--ref[p] > 0) return;
+    if (hashed[p]) push_cached(p);
+    else clean.push_back(p);
+  }
+  // the key of block i of a request whose pages are `pages`
+  BlockKey make_key(const std::vector<int32_t>& pages, const std::vector<int32_t>& tokens, int32_t i) const {
+    BlockKey k;
+    if (i > 0) {
+      k.parent = pages[i - 1];
+      k.parent_gen = gen[k.parent];
+    }
+    std::memcpy(k.tok, tokens.data() + (size_t)i * CB_PAGE_SIZE, sizeof k.tok);
+    return k;
+  }
+};
+
 }  // namespace
 
 struct cb_builder {
   cb_builder_config cfg{};
-  std::vector<int32_t> free_list;       // stack; back() is handed out next
+  PagePool pool;
   std::vector<std::unique_ptr<Request>> reqs;  // arrival order
   std::unordered_map<int64_t, Request*> by_id;
   int64_t arrivals = 0;
   int64_t steps = 0;
   int64_t total_stalls = 0;
   int64_t total_finished = 0;
+  int64_t prefix_hit_tokens = 0;
 
   // step outputs (owned, valid until the next step)
   std::vector<int64_t> o_req_ids, o_finished, o_stalled;
   std::vector<int32_t> o_qsl, o_ctx, o_off, o_bt, o_slots;
 
-  int32_t take_page() {
-    int32_t p = free_list.back();
-    free_list.pop_back();
-    return p;
+  int32_t take_page() { return pool.take(); }
+  int32_t free_pages() const { return pool.free(); }
+
+  // registered blocks matching r's prompt, stopping short of its last token
+  void match(const Request& r, std::vector<int32_t>& out) const {
+    out.clear();
+    for (int32_t i = 0; i < (r.prompt_len - 1) / CB_PAGE_SIZE; ++i) {
+      auto it = pool.index.find(pool.make_key(out, r.tokens, i));
+      if (it == pool.index.end()) break;
+      out.push_back(it->second);
+    }
   }
-  int32_t free_pages() const { return (int32_t)free_list.size(); }
+  // register r's full prompt blocks, in order, until one is already known
+  void register_blocks(Request& r) {
+    const int32_t full = std::min(r.cached, r.prompt_len) / CB_PAGE_SIZE;
+    while (r.registered < full && !r.stop_registering) {
+      const int32_t i = r.registered;
+      BlockKey k = pool.make_key(r.pages, r.tokens, i);
+      if (pool.index.count(k)) {
+        r.stop_registering = true;
+        break;
+      }
+      const int32_t p = r.pages[i];
+      pool.index.emplace(k, p);
+      pool.key[p] = k;
+      pool.hashed[p] = 1;
+      r.registered++;
+    }
+  }
+  void copy_state_from(const cb_builder& o) {
+    cfg = o.cfg;
+    pool = o.pool;
+    arrivals = o.arrivals;
+    steps = o.steps;
+    total_stalls = o.total_stalls;
+    total_finished = o.total_finished;
+    prefix_hit_tokens = o.prefix_hit_tokens;
+    reqs.clear();
+    by_id.clear();
+    for (const auto& r : o.reqs) {
+      reqs.emplace_back(new Request(*r));
+      by_id[r->id] = reqs.back().get();
+    }
+  }
 };
 
 extern "C" {
@@ -79,17 +223,31 @@ int cb_builder_create(const cb_builder_config* config, cb_builder** out) {
     return cb::fail(CB_ERR_INVALID, "budgets and pool size must be positive (pool < 2^27 pages)");
   if (c.max_prefill_chunk < 0 || !(c.safety_margin >= 0.0f && c.safety_margin < 1.0f))
     return cb::fail(CB_ERR_INVALID, "max_prefill_chunk must be >= 0 and safety_margin in [0, 1)");
+  if (c.policy != CB_POLICY_FIFO && c.policy != CB_POLICY_PREFILL_FIRST)
+    return cb::fail(CB_ERR_INVALID, "unknown scheduling policy %d", c.policy);
+  if (c.max_partial_prefills < 0 || c.max_long_partial_prefills < 0 || c.long_prefill_threshold < 0)
+    return cb::fail(CB_ERR_INVALID, "prefill caps and the long-prompt threshold must be >= 0");
   cb_builder* b = new (std::nothrow) cb_builder();
   if (!b) return cb::fail(CB_ERR_INVALID, "out of host memory");
   b->cfg = c;
-  b->free_list.resize(c.num_pages);
-  for (int32_t i = 0; i < c.num_pages; ++i) b->free_list[i] = c.num_pages - 1 - i;
+  PagePool& pool = b->pool;
+  pool.clean.resize(c.num_pages);
+  for (int32_t i = 0; i < c.num_pages; ++i) pool.clean[i] = c.num_pages - 1 - i;
   if (c.page_shuffle_seed != 0) {
     uint64_t st = c.page_shuffle_seed;
     for (int32_t i = c.num_pages - 1; i > 0; --i) {
       int32_t j = (int32_t)(splitmix64(st) % (uint64_t)(i + 1));
-      std::swap(b->free_list[i], b->free_list[j]);
+      std::swap(pool.clean[i], pool.clean[j]);
     }
+  }
+  if (c.allow_block_sharing) {
+    pool.sharing = true;
+    pool.ref.assign(c.num_pages, 0);
+    pool.gen.assign(c.num_pages, 0);
+    pool.hashed.assign(c.num_pages, 0);
+    pool.key.resize(c.num_pages);
+    pool.prev.assign(c.num_pages, -1);
+    pool.next.assign(c.num_pages, -1);
   }
   *out = b;
   return CB_OK;
@@ -100,25 +258,15 @@ int cb_builder_clone(const cb_builder* b, cb_builder** out) {
   if (!b || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_clone: null argument");
   cb_builder* c = new (std::nothrow) cb_builder();
   if (!c) return cb::fail(CB_ERR_INVALID, "out of host memory");
-  c->cfg = b->cfg;
-  c->free_list = b->free_list;
-  c->arrivals = b->arrivals;
-  c->steps = b->steps;
-  c->total_stalls = b->total_stalls;
-  c->total_finished = b->total_finished;
-  for (const auto& r : b->reqs) {
-    c->reqs.emplace_back(new Request(*r));
-    c->by_id[r->id] = c->reqs.back().get();
-  }
+  c->copy_state_from(*b);
   *out = c;
   return CB_OK;
 }
 
 void cb_builder_destroy(cb_builder* b) { delete b; }
 
-int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t output_len,
-                      int32_t tokens_cached) {
-  cb::clear_error();
+static int submit_impl(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t output_len,
+                       int32_t tokens_cached, const int32_t* tokens) {
   if (!b) return cb::fail(CB_ERR_INVALID, "cb_builder_submit: null builder");
   if (b->by_id.count(req_id)) return cb::fail(CB_ERR_INVALID, "duplicate request id %lld", (long long)req_id);
   if (prompt_len < 1 || output_len < 1 || tokens_cached < 0)
@@ -134,6 +282,7 @@ int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t
   r->prompt_len = prompt_len;
   r->output_len = output_len;
   r->arrival = b->arrivals;
+  if (tokens && b->pool.sharing) r->tokens.assign(tokens, tokens + prompt_len);
   if (tokens_cached > 0) {
     int32_t need = (int32_t)cb::ceil_div(tokens_cached, CB_PAGE_SIZE);
     if (need > b->free_pages())
@@ -154,10 +303,24 @@ int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t
   return CB_OK;
 }
 
+int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t output_len,
+                      int32_t tokens_cached) {
+  cb::clear_error();
+  return submit_impl(b, req_id, prompt_len, output_len, tokens_cached, nullptr);
+}
+
+int cb_builder_submit_tokens(cb_builder* b, int64_t req_id, const int32_t* tokens, int32_t prompt_len,
+                             int32_t output_len) {
+  cb::clear_error();
+  if (!tokens) return cb::fail(CB_ERR_INVALID, "cb_builder_submit_tokens: null token array");
+  return submit_impl(b, req_id, prompt_len, output_len, 0, tokens);
+}
+
 int cb_builder_step(cb_builder* b, cb_step* out) {
   cb::clear_error();
   if (!b || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_step: null argument");
   const cb_builder_config& c = b->cfg;
+  PagePool& pool = b->pool;
   b->o_req_ids.clear();
   b->o_finished.clear();
   b->o_stalled.clear();
@@ -168,7 +331,7 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
     keep.reserve(b->reqs.size());
     for (auto& r : b->reqs) {
       if (r->state == State::Finished) {
-        for (int32_t p : r->pages) b->free_list.push_back(p);
+        for (int32_t p : r->pages) pool.release(p);
         b->o_finished.push_back(r->id);
         b->by_id.erase(r->id);
         b->total_finished++;
@@ -183,55 +346,97 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
   std::vector<Pick> picks;
   int32_t tokens_left = c.max_batch_tokens;
   int32_t slots_left = c.max_requests_per_batch;
-  int32_t new_pages = 0;
+  int32_t new_pages = 0, step_hits = 0, n_prefills = 0, n_long = 0;
+  auto room = [&] { return tokens_left >= 1 && slots_left >= 1; };
+  auto is_long = [&](const Request* r) { return r->prompt_len > c.long_prefill_threshold; };
+  auto capped = [&](const Request* r) {
+    if (c.max_partial_prefills > 0 && n_prefills >= c.max_partial_prefills) return true;
+    return c.max_long_partial_prefills > 0 && is_long(r) && n_long >= c.max_long_partial_prefills;
+  };
+  auto pick_prefill = [&](Request* r, int32_t n) {
+    picks.push_back({r, n, false});
+    tokens_left -= n;
+    slots_left -= 1;
+    n_prefills++;
+    n_long += is_long(r) ? 1 : 0;
+  };
 
-  // 1. active decodes, one token each
-  for (auto& up : b->reqs) {
-    Request* r = up.get();
-    if (r->state != State::Decoding) continue;
-    if (tokens_left < 1 || slots_left < 1) break;
-    int32_t need = (r->cached % CB_PAGE_SIZE == 0) ? 1 : 0;
-    if (need > b->free_pages()) { b->o_stalled.push_back(r->id); continue; }
-    if (need) { r->pages.push_back(b->take_page()); new_pages++; }
-    picks.push_back({r, 1, true});
-    tokens_left -= 1;
-    slots_left -= 1;
+  // active decodes, one token each
+  auto decodes = [&] {
+    for (auto& up : b->reqs) {
+      Request* r = up.get();
+      if (r->state != State::Decoding) continue;
+      if (!room()) break;
+      int32_t need = (r->cached % CB_PAGE_SIZE == 0) ? 1 : 0;
+      if (need > b->free_pages()) { b->o_stalled.push_back(r->id); continue; }
+      if (need) { r->pages.push_back(b->take_page()); new_pages++; }
+      picks.push_back({r, 1, true});
+      tokens_left -= 1;
+      slots_left -= 1;
+    }
+  };
+  // active prefills, each taking every token that still fits
+  auto active_prefills = [&] {
+    for (auto& up : b->reqs) {
+      Request* r = up.get();
+      if (r->state != State::Prefilling) continue;
+      if (!room()) break;
+      if (capped(r)) continue;
+      int64_t chunk = std::min<int64_t>(r->prompt_len - r->cached, tokens_left);
+      if (c.max_prefill_chunk > 0) chunk = std::min<int64_t>(chunk, c.max_prefill_chunk);
+      chunk = std::min<int64_t>(chunk, ((int64_t)r->pages.size() + b->free_pages()) * CB_PAGE_SIZE - r->cached);
+      if (chunk <= 0) { b->o_stalled.push_back(r->id); continue; }
+      int32_t need = (int32_t)(cb::ceil_div(r->cached + chunk, CB_PAGE_SIZE) - (int64_t)r->pages.size());
+      for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
+      new_pages += need;
+      pick_prefill(r, (int32_t)chunk);
+    }
+  };
+  // waiting requests, arrival order, strict head of line on pages
+  std::vector<int32_t> matched;
+  auto waiting = [&] {
+    for (auto& up : b->reqs) {
+      Request* r = up.get();
+      if (r->state != State::Waiting) continue;
+      if (!room()) break;
+      if (capped(r)) continue;
+      matched.clear();
+      if (pool.sharing && !r->tokens.empty()) b->match(*r, matched);
+      const int32_t start = (int32_t)matched.size() * CB_PAGE_SIZE;
+      int32_t chunk = std::min(r->prompt_len - start, tokens_left);
+      if (c.max_prefill_chunk > 0) chunk = std::min(chunk, c.max_prefill_chunk);
+      int32_t reused = 0;
+      for (int32_t p : matched) reused += pool.ref[p] == 0 ? 1 : 0;
+      const int32_t fresh = (int32_t)cb::ceil_div(chunk, CB_PAGE_SIZE);
+      const int32_t need = fresh + reused;
+      if (need > b->free_pages()) break;
+      if (c.safety_margin > 0.0f &&
+          (double)(b->free_pages() - need) < (double)c.safety_margin * (double)c.num_pages)
+        break;
+      for (int32_t p : matched) {
+        if (pool.ref[p] == 0) pool.unlink(p);
+        pool.ref[p]++;
+      }
+      r->pages.assign(matched.begin(), matched.end());
+      for (int32_t i = 0; i < fresh; ++i) r->pages.push_back(b->take_page());
+      r->cached = start;
+      r->registered = (int32_t)matched.size();
+      r->state = State::Prefilling;
+      new_pages += need;
+      step_hits += start;
+      pick_prefill(r, chunk);
+    }
+  };
+  if (c.policy == CB_POLICY_PREFILL_FIRST) {
+    active_prefills();
+    decodes();
+  } else {
+    decodes();
+    active_prefills();
   }
-  // 2. active prefills, each taking every token that still fits
-  for (auto& up : b->reqs) {
-    Request* r = up.get();
-    if (r->state != State::Prefilling) continue;
-    if (tokens_left < 1 || slots_left < 1) break;
-    int64_t chunk = std::min<int64_t>(r->prompt_len - r->cached, tokens_left);
-    if (c.max_prefill_chunk > 0) chunk = std::min<int64_t>(chunk, c.max_prefill_chunk);
-    chunk = std::min<int64_t>(chunk, ((int64_t)r->pages.size() + b->free_pages()) * CB_PAGE_SIZE - r->cached);
-    if (chunk <= 0) { b->o_stalled.push_back(r->id); continue; }
-    int32_t need = (int32_t)(cb::ceil_div(r->cached + chunk, CB_PAGE_SIZE) - (int64_t)r->pages.size());
-    for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
-    new_pages += need;
-    picks.push_back({r, (int32_t)chunk, false});
-    tokens_left -= (int32_t)chunk;
-    slots_left -= 1;
-  }
-  // 3. waiting requests, arrival order, strict head of line
-  for (auto& up : b->reqs) {
-    Request* r = up.get();
-    if (r->state != State::Waiting) continue;
-    if (tokens_left < 1 || slots_left < 1) break;
-    int32_t chunk = std::min(r->prompt_len, tokens_left);
-    if (c.max_prefill_chunk > 0) chunk = std::min(chunk, c.max_prefill_chunk);
-    int32_t need = (int32_t)cb::ceil_div(chunk, CB_PAGE_SIZE);
-    if (need > b->free_pages()) break;
-    if (c.safety_margin > 0.0f &&
-        (double)(b->free_pages() - need) < (double)c.safety_margin * (double)c.num_pages)
-      break;
-    for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
-    new_pages += need;
-    r->state = State::Prefilling;
-    picks.push_back({r, chunk, false});
-    tokens_left -= chunk;
-    slots_left -= 1;
-  }
+  waiting();
+  // the descriptor lists decodes first, each class in picking order
+  std::stable_partition(picks.begin(), picks.end(), [](const Pick& p) { return p.decode; });
 
   // emit the descriptor
   const int32_t n = (int32_t)picks.size();
@@ -269,10 +474,12 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
     else if (r->cached == r->prompt_len) r->generated = 1;
     if (r->generated >= 1)
       r->state = (r->generated >= r->output_len) ? State::Finished : State::Decoding;
+    if (pool.sharing && !r->tokens.empty()) b->register_blocks(*r);
   }
   b->o_qsl[n] = t;
   b->steps++;
   b->total_stalls += (int64_t)b->o_stalled.size();
+  b->prefix_hit_tokens += step_hits;
 
   out->num_seqs = n;
   out->num_decodes = num_decodes;
@@ -283,6 +490,7 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
   out->num_finished = (int32_t)b->o_finished.size();
   out->num_stalled = (int32_t)b->o_stalled.size();
   out->new_pages = new_pages;
+  out->prefix_hit_tokens = step_hits;
   out->req_ids = b->o_req_ids.data();
   out->query_start_loc = b->o_qsl.data();
   out->context_lens = b->o_ctx.data();
@@ -319,7 +527,17 @@ int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out) {
       case State::Decoding: out->num_decoding++; break;
       case State::Finished: out->num_finished_pending++; break;
     }
-    out->used_slots += r->cached;
+    if (!b->pool.sharing) out->used_slots += r->cached;
+  }
+  if (b->pool.sharing) {  // a shared page counts once, at its fill
+    std::unordered_map<int32_t, int32_t> fill;
+    for (const auto& r : b->reqs)
+      for (size_t i = 0; i < r->pages.size(); ++i) {
+        const int32_t f = std::max(0, std::min<int32_t>(CB_PAGE_SIZE, r->cached - (int32_t)i * CB_PAGE_SIZE));
+        int32_t& v = fill[r->pages[i]];
+        v = std::max(v, f);
+      }
+    for (const auto& kv : fill) out->used_slots += kv.second;
   }
   out->allocated_slots = (int64_t)(b->cfg.num_pages - b->free_pages()) * CB_PAGE_SIZE;
   out->steps = b->steps;
@@ -327,6 +545,8 @@ int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out) {
   out->total_finished = b->total_finished;
   out->fragmentation = out->allocated_slots > 0
       ? (double)(out->allocated_slots - out->used_slots) / (double)out->allocated_slots : 0.0;
+  out->prefix_hit_tokens = b->prefix_hit_tokens;
+  out->cached_pages = b->pool.cached;
   return CB_OK;
 }
 
@@ -336,18 +556,7 @@ namespace cb {
 int builder_assign(cb_builder* dst, const cb_builder* src) {
   if (!dst || !src) return fail(CB_ERR_INVALID, "builder_assign: null argument");
   if (dst == src) return CB_OK;
-  dst->cfg = src->cfg;
-  dst->free_list = src->free_list;
-  dst->arrivals = src->arrivals;
-  dst->steps = src->steps;
-  dst->total_stalls = src->total_stalls;
-  dst->total_finished = src->total_finished;
-  dst->reqs.clear();
-  dst->by_id.clear();
-  for (const auto& r : src->reqs) {
-    dst->reqs.emplace_back(new Request(*r));
-    dst->by_id[r->id] = dst->reqs.back().get();
-  }
+  dst->copy_state_from(*src);
   return CB_OK;
 }
 

@@ -21,8 +21,8 @@ import ctypes as C
 
 import numpy as np
 
-from . import Builder, Step, kv_append, CB_BF16, CB_F32, PAGE_SIZE
-from ._lib import BuilderConfig, EngineConfig, StepDesc, CbError, check, load, CB_ERR_CAPACITY, CB_ERR_WORKSPACE
+from . import Builder, Step, builder_config, kv_append, CB_BF16, CB_F32, PAGE_SIZE
+from ._lib import EngineConfig, StepDesc, CbError, check, load, CB_ERR_CAPACITY, CB_ERR_WORKSPACE
 
 
 def _arr(ptr, n, dtype):
@@ -91,7 +91,8 @@ class PagedAttentionLayer:
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, num_pages: int,
                  max_batch_tokens: int, max_requests_per_batch: int, dtype: str = "bf16",
                  max_prefill_chunk: int = 0, safety_margin: float = 0.0, page_shuffle_seed: int = 0,
-                 device=None, cache_fill: float = 0.0, meta_pages_per_request: int = 2048):
+                 device=None, cache_fill: float = 0.0, meta_pages_per_request: int = 2048,
+                 **policy_kw):
         import torch
         self.torch = torch
         self._lib = load()
@@ -109,8 +110,9 @@ class PagedAttentionLayer:
         slot_ints = 3 * B + 1 + T + B * min(num_pages, meta_pages_per_request) + 64
         self._alloc_meta(2 * slot_ints)
         self._ws = None
-        cfg = EngineConfig(BuilderConfig(max_batch_tokens, max_requests_per_batch, num_pages, PAGE_SIZE,
-                                         max_prefill_chunk, safety_margin, page_shuffle_seed),
+        cfg = EngineConfig(builder_config(max_batch_tokens, max_requests_per_batch, num_pages,
+                                          max_prefill_chunk, safety_margin, page_shuffle_seed,
+                                          **policy_kw),
                            num_q_heads, num_kv_heads, head_dim, self.code, self.scale,
                            self.k_cache.data_ptr(), self.v_cache.data_ptr(), self._meta_dev.data_ptr(),
                            self._meta_host.data_ptr(), self._meta_dev.numel() * 4, None, 0)

@@ -21,10 +21,14 @@
  *            prompts fill the remaining token budget.
  *   [CBA]    Hugging Face transformers, "Continuous batching architecture":
  *            sections "Request lifecycle", "Chunked prefill", "Scheduler",
- *            "FIFO", "Memory management", "Admission".
+ *            "FIFO", "PrefillFirst", "Memory management", "Admission",
+ *            "Prefix caching" and the release of cached blocks under
+ *            "Eviction".
  *   [VLLM]   AI Engineering from Scratch, "vLLM serving internals": sections
  *            "PagedAttention as virtual memory" (16-token blocks, per-sequence
  *            block tables) and "What the scheduler looks like".
+ *   [TNG]    TNG blog post on prefill/decode interference, "Request-parallel
+ *            prefill": several prefills per step, few of them long.
  *
  * Conventions for every call:
  *   - No call allocates device memory, synchronises the device or blocks on
@@ -212,6 +216,13 @@ int cb_profile_events(void* start_event, void* stop_event);
  * ------------------------------------------------------------------------- */
 typedef struct cb_builder cb_builder;
 
+/* Scheduling policies.  [CBA] "FIFO": active decodes, then active prefills,
+ * then waiting requests.  [CBA] "PrefillFirst": split prefills are carried to
+ * completion before decoding resumes -- here active prefills are picked
+ * first, then active decodes, then waiting requests.  Under both the step
+ * lists its decodes first. */
+enum { CB_POLICY_FIFO = 0, CB_POLICY_PREFILL_FIRST = 1 };
+
 typedef struct {
   int32_t max_batch_tokens;       /* >= 1 */
   int32_t max_requests_per_batch; /* >= 1 */
@@ -221,6 +232,18 @@ typedef struct {
   float safety_margin;            /* in [0, 1); 0 disables the margin */
   uint64_t page_shuffle_seed;     /* 0: pages handed out 0, 1, 2, ...; else the
                                      initial free list is a seeded permutation */
+  int32_t policy;                 /* CB_POLICY_* */
+  /* [TNG] request-parallel prefill: prefill chunks per step (0 = no cap) and,
+   * among them, chunks of prompts longer than long_prefill_threshold tokens
+   * (0 = no cap).  A prefill over a cap is skipped, not stalled, and the
+   * requests behind it are still considered. */
+  int32_t max_partial_prefills;
+  int32_t max_long_partial_prefills;
+  int32_t long_prefill_threshold;
+  /* [CBA] "Prefix caching": nonzero lets requests submitted with their prompt
+   * tokens (cb_builder_submit_tokens) reuse registered full prompt blocks;
+   * see cb_builder_submit_tokens. */
+  int32_t allow_block_sharing;
 } cb_builder_config;
 
 /* The step descriptor.  Arrays are owned by the builder and stay valid until
@@ -234,7 +257,8 @@ typedef struct {
   int32_t block_table_stride; /* max pages held by a scheduled sequence (>= 1) */
   int32_t num_finished;       /* released at the start of this step */
   int32_t num_stalled;
-  int32_t new_pages;          /* pages allocated this step */
+  int32_t new_pages;          /* pages taken from the free pool this step */
+  int32_t prefix_hit_tokens;  /* prompt tokens reused from shared blocks this step */
   const int64_t* req_ids;         /* [num_seqs] */
   const int32_t* query_start_loc; /* [num_seqs + 1] */
   const int32_t* context_lens;    /* [num_seqs] */
@@ -258,6 +282,8 @@ typedef struct {
   int64_t total_stalls;
   int64_t total_finished;
   double fragmentation;         /* (allocated - used) / allocated; 0 if none */
+  int64_t prefix_hit_tokens;    /* prompt tokens reused from shared blocks so far */
+  int32_t cached_pages;         /* free pages still holding a registered block */
 } cb_builder_stats;
 
 /* Create a builder.  Errors: CB_ERR_INVALID (null, bad budget or margin),
@@ -280,6 +306,23 @@ void cb_builder_destroy(cb_builder* b);
  * pages are not free). */
 int cb_builder_submit(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_t output_len,
                       int32_t tokens_cached);
+
+/* Submit a new request together with its prompt tokens (host array of
+ * prompt_len ids, copied).  With allow_block_sharing set, at admission the
+ * request reuses the longest chain of registered full blocks that matches
+ * its prompt, stopping short of the last prompt token (always computed), and
+ * its first chunk starts at the matched offset.  A block's identity is its 16
+ * tokens together with the block before it; blocks wholly inside the prompt
+ * are registered, in order, when the step that fills them is built, until
+ * the first one whose identity is already registered.  Shared pages are
+ * reference counted; a released registered block stays matchable until an
+ * allocation finds no page without a registration and takes the most
+ * recently released one.  Reused pages that no request held count against
+ * the free pages at admission.  Without sharing this is cb_builder_submit
+ * with tokens_cached = 0.
+ * Errors: as cb_builder_submit, and CB_ERR_INVALID for a null token array. */
+int cb_builder_submit_tokens(cb_builder* b, int64_t req_id, const int32_t* tokens, int32_t prompt_len,
+                             int32_t output_len);
 
 /* Run the scheduler for one engine step and fill *out.  A step with nothing
  * schedulable returns CB_OK with num_seqs == 0. */

@@ -412,7 +412,16 @@ class Scheduler:
         return self.num_pages - self.free
 
     def used_slots(self) -> int:
-        return sum(r.cached for r in self.requests.values())
+        """Cached tokens held in pages; a shared block counts once."""
+        total, shared = 0, {}
+        for r in self.requests.values():
+            for i, e in enumerate(r.blocks):
+                fill = max(0, min(self.page, r.cached - i * self.page))
+                if e is None:
+                    total += fill
+                else:
+                    shared[id(e)] = max(shared.get(id(e), 0), fill)
+        return total + sum(shared.values())
 
     def idle(self) -> bool:
         return not self.requests

@@ -16,12 +16,17 @@ from oracle import paging
 import workloads as wl
 
 
+POLICY_KEYS = ("policy", "max_partial_prefills", "max_long_partial_prefills", "long_prefill_threshold",
+               "allow_block_sharing")
+
+
 def _pair(**kw):
+    pol = {k: kw[k] for k in POLICY_KEYS if k in kw}
     o = FifoScheduler(kw["max_batch_tokens"], kw["max_requests"], kw["num_pages"],
-                      max_prefill_chunk=kw.get("chunk", 0), safety_margin=kw.get("margin", 0.0))
+                      max_prefill_chunk=kw.get("chunk", 0), safety_margin=kw.get("margin", 0.0), **pol)
     b = cb.Builder(kw["max_batch_tokens"], kw["max_requests"], kw["num_pages"],
                    max_prefill_chunk=kw.get("chunk", 0), safety_margin=kw.get("margin", 0.0),
-                   page_shuffle_seed=kw.get("shuffle", 0))
+                   page_shuffle_seed=kw.get("shuffle", 0), **pol)
     return o, b
 
 
@@ -35,7 +40,10 @@ def _compare_step(so, sb, tables):
     assert sorted(so.finished) == sorted(sb.finished_ids.tolist())
     assert so.stalled == sb.stalled_ids.tolist()
     assert so.new_pages == sb.new_pages
+    assert sum(x.prefix_hit for x in so.seqs) == sb.prefix_hit_tokens
     held = {}
+    serial_of = {}   # physical page -> oracle block serial (a page may be shared only as one block)
+    page_of = {}
     for s, x in enumerate(so.seqs):
         row = sb.block_tables[s, :x.pages]
         assert (sb.block_tables[s, x.pages:] == 0).all()
@@ -45,9 +53,15 @@ def _compare_step(so, sb, tables):
         tables[x.req_id] = row.copy()
         a, e = sb.query_start_loc[s], sb.query_start_loc[s + 1]
         assert np.array_equal(sb.slot_mapping[a:e], paging.slots_for(row, x.q_offset, x.context_len))
-        for pg in row.tolist():
-            assert pg not in held, "page shared by two requests"
-            held[pg] = x.req_id
+        for i, pg in enumerate(row.tolist()):
+            ser = x.blocks[i] if x.blocks else -1
+            if ser < 0:
+                assert pg not in held, "private page held twice"
+                held[pg] = x.req_id
+                continue
+            assert held.get(pg, None) is None or serial_of.get(pg) == ser, "page held twice"
+            assert serial_of.setdefault(pg, ser) == ser and page_of.setdefault(ser, pg) == pg
+            held[pg] = None   # shared block: consistent with the oracle's identity
     for rid in so.finished:
         tables.pop(rid, None)
 
@@ -144,3 +158,57 @@ def test_builder_errors():
     assert e.value.status == -1
     with pytest.raises(cb.CbError):
         b.block_table(99)
+
+
+def _prompt_family(rng, n):
+    """A few base prompts; each request takes a prefix of one and appends its own tail."""
+    return [rng.integers(0, 40, int(rng.integers(8, 160))).tolist() for _ in range(n)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_policies_caps_and_sharing_match_oracle(seed):
+    rng = np.random.default_rng(500 + seed)
+    kw = dict(max_batch_tokens=int(rng.integers(16, 300)), max_requests=int(rng.integers(1, 12)),
+              num_pages=int(rng.integers(30, 140)), chunk=int(rng.choice([0, 0, 16, 40])),
+              margin=float(rng.choice([0.0, 0.15])), shuffle=seed,
+              policy=str(rng.choice(["fifo", "prefill_first"])),
+              max_partial_prefills=int(rng.choice([0, 1, 2, 4])),
+              max_long_partial_prefills=int(rng.choice([0, 1])),
+              long_prefill_threshold=int(rng.choice([0, 60, 120])),
+              allow_block_sharing=bool(seed % 4 != 3))
+    o, b = _pair(**kw)
+    base = _prompt_family(rng, 3)
+    tables = {}
+    nid = 0
+    for step in range(400):
+        for _ in range(int(rng.poisson(0.7))):
+            fam = base[int(rng.integers(0, len(base)))]
+            n = int(rng.integers(1, len(fam) + 1))
+            if rng.random() < 0.3 and len(fam) >= 16:        # block-aligned prompts, often repeated
+                n = max(16, n - n % 16)
+            tail = 0 if rng.random() < 0.3 else int(rng.integers(0, 30))
+            toks = fam[:n] + rng.integers(0, 40, tail).tolist()
+            q = int(rng.integers(1, 30))
+            with_tokens = rng.random() < 0.8
+            cached = 0 if with_tokens or rng.random() < 0.8 else int(rng.integers(0, len(toks) + q - 1))
+            err_o = err_b = None
+            try:
+                o.submit(nid, len(toks), q, cached, tokens=toks if with_tokens else None)
+            except SchedulerError as e:
+                err_o = e.kind
+            try:
+                b.submit(nid, len(toks), q, cached, tokens=toks if with_tokens else None)
+            except cb.CbError as e:
+                err_b = {-1: "invalid", -5: "capacity"}[e.status]
+            assert err_o == err_b
+            nid += 1
+        so, sb = o.step(), b.step()
+        _compare_step(so, sb, tables)
+        st = b.stats()
+        assert st["free_pages"] == o.free
+        assert st["cached_pages"] == len(o.cached)
+        assert st["used_slots"] == o.used_slots()
+        assert st["prefix_hit_tokens"] == o.prefix_hit_tokens
+    assert b.stats()["total_stalls"] == o.total_stalls
+    if kw["allow_block_sharing"]:
+        assert o.prefix_hit_tokens > 0
