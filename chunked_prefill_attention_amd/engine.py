@@ -46,6 +46,7 @@ class StepView:
         self.num_seqs, self.num_decodes, self.num_tokens = d.num_seqs, d.num_decodes, d.num_tokens
         self.max_query_len, self.max_context_len = d.max_query_len, d.max_context_len
         self.block_table_stride, self.new_pages = d.block_table_stride, d.new_pages
+        self.prefix_hit_tokens = d.prefix_hit_tokens
         self._cache = {}
 
     def _get(self, name, n, dtype):

@@ -71,6 +71,29 @@ def seq_kv(seed: int, seq: int, start: int, end: int, n_kv_heads: int, head_dim:
     return _finish(np.ascontiguousarray(k), dtype), _finish(np.ascontiguousarray(v), dtype)
 
 
+def prompt_kv(seed: int, req_id: int, tokens, end: int, n_kv_heads: int, head_dim: int, dtype: str):
+    """K, V ``[end, Hkv, D]`` of a request whose prompt is ``tokens``.
+
+    Row ``p < len(tokens)`` is drawn from a seed made of the whole prompt prefix
+    ``tokens[:p+1]`` (a 64-bit FNV-1a chain), so requests that share a prefix
+    hold identical rows there and different prefixes give different rows; rows
+    past the prompt depend on the request.
+    """
+    k = np.empty((end, n_kv_heads, head_dim), np.float32)
+    v = np.empty_like(k)
+    h = 0xCBF29CE484222325
+    for p in range(end):
+        if p < len(tokens):
+            h = ((h ^ (int(tokens[p]) & 0xFFFFFFFF)) * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+            key = (seed, 7, h & 0xFFFFFFFF, h >> 32, p)
+        else:
+            key = (seed, 8, req_id, p)
+        g = _rng(*key)
+        k[p] = g.standard_normal(size=(n_kv_heads, head_dim), dtype=np.float32)
+        v[p] = g.standard_normal(size=(n_kv_heads, head_dim), dtype=np.float32)
+    return _finish(k, dtype), _finish(v, dtype)
+
+
 def seq_q(seed: int, seq: int, start: int, end: int, n_q_heads: int, head_dim: int,
           dtype: str, std: float = 1.0):
     """Q ``[end-start, Hq, D]`` of tokens ``start..end-1`` of sequence ``seq``."""
