@@ -30,6 +30,13 @@ Readings of points the pages leave open (each also listed in the design doc):
 * grouped-query attention (absent from the pages) uses contiguous groups:
   query head ``h`` reads KV head ``h // (Hq // Hkv)``.
 
+Sliding window (Hugging Face transformers, "Continuous batching
+architecture", section "Memory management": sliding-attention layers keep only
+a fixed window of the most recent tokens).  With a window of ``W`` tokens the
+row at position ``p`` sees keys ``j`` with ``p - W < j <= p`` (the ``W`` most
+recent positions, itself included); ``W = 0`` means no window.  Reading: the
+window counts the query's own position, so ``W = 1`` sees only itself.
+
 Two forms are given.  ``attend_rows`` is the definition taken row by row: a
 row's arithmetic depends only on that row's query and on keys ``0..p``, so
 chunked and one-shot prefill agree bit for bit.  ``attend`` is the same
@@ -60,22 +67,28 @@ def _check(q, k, v):
     return L, Hq, D, ctx, Hkv
 
 
-def attend_row(q_row, k, v, pos: int, kv_head: int, scale: float) -> np.ndarray:
-    """One query row at absolute position ``pos`` against keys ``0..pos``.
+def _first_key(pos: int, window: int) -> int:
+    return max(0, pos - window + 1) if window > 0 else 0
+
+
+def attend_row(q_row, k, v, pos: int, kv_head: int, scale: float, window: int = 0) -> np.ndarray:
+    """One query row at absolute position ``pos`` against keys ``0..pos``
+    (``pos-window+1 .. pos`` with a sliding window).
 
     ``q_row`` is ``[D]``; ``k, v`` are ``[ctx, Hkv, D]``.  Returns ``[D]``.
     This is the five-line definition in the module docstring, nothing else.
     """
+    lo = _first_key(pos, window)
     qr = _as64(q_row)
-    kk = _as64(k[: pos + 1, kv_head, :])      # keys 0..pos (inclusive)
-    vv = _as64(v[: pos + 1, kv_head, :])
+    kk = _as64(k[lo: pos + 1, kv_head, :])    # keys lo..pos (inclusive)
+    vv = _as64(v[lo: pos + 1, kv_head, :])
     x = scale * (kk @ qr)                      # x_j, j = 0..pos
     m = x.max()
     w = np.exp(x - m)
     return (w @ vv) / w.sum()
 
 
-def attend_rows(q, k, v, scale: float, rows=None) -> np.ndarray:
+def attend_rows(q, k, v, scale: float, rows=None, window: int = 0) -> np.ndarray:
     """Row-by-row form.  ``q[L, Hq, D]``, ``k, v[ctx, Hkv, D]`` -> ``[L, Hq, D]``.
 
     ``rows`` optionally restricts the work to a list of ``(i, h)`` pairs;
@@ -87,23 +100,28 @@ def attend_rows(q, k, v, scale: float, rows=None) -> np.ndarray:
     out = np.full((L, Hq, D), np.nan)
     todo = rows if rows is not None else [(i, h) for i in range(L) for h in range(Hq)]
     for i, h in todo:
-        out[i, h] = attend_row(q[i, h], k, v, off + i, h // G, scale)
+        out[i, h] = attend_row(q[i, h], k, v, off + i, h // G, scale, window)
     return out
 
 
-def attend(q, k, v, scale: float) -> np.ndarray:
+def attend(q, k, v, scale: float, window: int = 0) -> np.ndarray:
     """Matrix form of the same definition.  Shapes as ``attend_rows``.
 
     For each query head: scores ``S = scale * Q K^T`` over the whole history,
-    entries with key position > query position set to -inf, a softmax along
-    each row, then ``P V``.
+    entries with key position > query position (or, with a window, at or
+    below query position - window) set to -inf, a softmax along each row,
+    then ``P V``.  Masked entries are replaced, never multiplied, so values
+    outside a row's keys cannot reach it.
     """
     L, Hq, D, ctx, Hkv = _check(q, k, v)
     G = Hq // Hkv
     off = ctx - L
     q64, k64, v64 = _as64(q), _as64(k), _as64(v)
     pos = off + np.arange(L)
-    visible = np.arange(ctx)[None, :] <= pos[:, None]          # [L, ctx]
+    j = np.arange(ctx)[None, :]
+    visible = j <= pos[:, None]                                # [L, ctx]
+    if window > 0:
+        visible &= j > pos[:, None] - window
     out = np.empty((L, Hq, D))
     for h in range(Hq):
         g = h // G
@@ -111,15 +129,18 @@ def attend(q, k, v, scale: float) -> np.ndarray:
         s = np.where(visible, s, -np.inf)
         m = s.max(axis=1, keepdims=True)
         w = np.exp(s - m)                                      # masked -> 0
-        out[:, h, :] = (w @ v64[:, g, :]) / w.sum(axis=1, keepdims=True)
+        vg = v64[:, g, :]
+        if window > 0:   # keys below every row's window may hold anything
+            vg = np.where(visible.any(axis=0)[:, None], vg, 0.0)
+        out[:, h, :] = (w @ vg) / w.sum(axis=1, keepdims=True)
     return out
 
 
-def attend_step(seqs, scale: float, rows_only=False):
+def attend_step(seqs, scale: float, rows_only=False, window: int = 0):
     """Whole engine step: a list of per-sequence ``(q, k_hist, v_hist)``.
 
     Returns a list of ``[L_s, Hq, D]`` fp64 outputs in the same order.  Each
     sequence is independent (the step is a batch of independent requests).
     """
     f = attend_rows if rows_only else attend
-    return [f(q, k, v, scale) for (q, k, v) in seqs]
+    return [f(q, k, v, scale, window=window) for (q, k, v) in seqs]

@@ -219,3 +219,106 @@ def test_rejects_bad_shapes():
         ora.attend(np.zeros((3, 3, 4)), np.zeros((5, 2, 4)), np.zeros((5, 2, 4)), 1.0)
     with pytest.raises(ValueError):
         ora.attend(np.zeros((6, 2, 4)), np.zeros((5, 2, 4)), np.zeros((5, 2, 4)), 1.0)
+
+
+# -- sliding window ---------------------------------------------------------------
+
+def _sdpa64_window(q, k, v, scale, window):
+    """torch SDPA in float64 with the band mask p - W < j <= p."""
+    L, Hq, D = q.shape
+    ctx, Hkv, _ = k.shape
+    G = Hq // Hkv
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2))).double()[None]
+    kt = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2))).double().repeat_interleave(G, 0)[None]
+    vt = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2))).double().repeat_interleave(G, 0)[None]
+    start = ctx - L
+    band = torch.ones(L, ctx, dtype=torch.bool).tril(diagonal=start) & \
+        ~torch.ones(L, ctx, dtype=torch.bool).tril(diagonal=start - window)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=band, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _brute_window(q, k, v, scale, window):
+    L, Hq, D = q.shape
+    ctx, Hkv, _ = k.shape
+    G = Hq // Hkv
+    out = np.zeros((L, Hq, D))
+    for i in range(L):
+        p = ctx - L + i
+        for h in range(Hq):
+            g = h // G
+            keys = [j for j in range(ctx) if p - window < j <= p]
+            x = [scale * math.fsum(float(q[i, h, d]) * float(k[j, g, d]) for d in range(D)) for j in keys]
+            m = max(x)
+            w = [math.exp(t - m) for t in x]
+            sw = math.fsum(w)
+            for d in range(D):
+                out[i, h, d] = math.fsum(wj * float(v[j, g, d]) for wj, j in zip(w, keys)) / sw
+    return out
+
+
+@pytest.mark.parametrize("L,ctx,W", [(1, 9, 3), (5, 12, 4), (7, 7, 2), (6, 11, 16), (3, 10, 1)])
+def test_window_matches_brute_force_and_sdpa(L, ctx, W):
+    q, k, v = _rand((L, 4, 3), 1), _rand((ctx, 2, 3), 2), _rand((ctx, 2, 3), 3)
+    for f in (ora.attend, ora.attend_rows):
+        got = f(q, k, v, 0.6, window=W)
+        assert np.abs(got - _brute_window(q, k, v, 0.6, W)).max() <= 1e-13
+        assert np.abs(got - _sdpa64_window(q, k, v, 0.6, W)).max() <= 1e-12
+
+
+def test_window_at_least_context_is_full_attention_bitwise():
+    q, k, v = _rand((20, 4, 8), 4), _rand((50, 2, 8), 5), _rand((50, 2, 8), 6)
+    for W in (50, 51, 1000):
+        assert np.array_equal(ora.attend_rows(q, k, v, 0.3, window=W), ora.attend_rows(q, k, v, 0.3))
+        assert np.array_equal(ora.attend(q, k, v, 0.3, window=W), ora.attend(q, k, v, 0.3))
+
+
+def test_window_one_returns_own_value_exactly():
+    q, k, v = _rand((9, 4, 8), 7), _rand((30, 2, 8), 8), _rand((30, 2, 8), 9)
+    for f in (ora.attend, ora.attend_rows):
+        out = f(q, k, v, 0.5, window=1)
+        for i in range(9):
+            for h in range(4):
+                assert np.array_equal(out[i, h], v[21 + i, h // 2])
+
+
+def test_window_zero_query_gives_windowed_mean():
+    k, v = _rand((40, 1, 5), 10), _rand((40, 1, 5), 11)
+    q = np.zeros((10, 2, 5))
+    out = ora.attend(q, k, v, 0.7, window=6)
+    for i in range(10):
+        p = 30 + i
+        assert np.abs(out[i, 0] - v[p - 5:p + 1, 0].mean(axis=0)).max() <= 1e-14
+
+
+def test_window_row_equals_full_attention_on_its_window():
+    """A windowed row is the unwindowed definition on keys p-W+1..p, bit for bit."""
+    q, k, v = _rand((12, 4, 8), 12), _rand((64, 2, 8), 13), _rand((64, 2, 8), 14)
+    W = 9
+    out = ora.attend_rows(q, k, v, 0.4, window=W)
+    for i in (0, 5, 11):
+        p = 52 + i
+        for h in range(4):
+            ref = ora.attend_row(q[i, h], k[p - W + 1:], v[p - W + 1:], W - 1, h // 2, 0.4)
+            assert np.array_equal(out[i, h], ref)
+
+
+def test_window_chunked_equals_one_shot_bitwise():
+    q, k, v = _rand((60, 4, 8), 15), _rand((60, 2, 8), 16), _rand((60, 2, 8), 17)
+    full = ora.attend_rows(q, k, v, 0.25, window=13)
+    for size in (7, 16, 25):
+        parts = [ora.attend_rows(q[a:a + size], k[:a + size][:min(60, a + size)],
+                                 v[:min(60, a + size)], 0.25, window=13)
+                 for a in range(0, 60, size)]
+        assert np.array_equal(np.concatenate(parts), full)
+
+
+def test_window_ignores_values_below_every_row():
+    """Keys no row can see may hold anything, NaN included."""
+    q, k, v = _rand((4, 2, 8), 18), _rand((40, 1, 8), 19), _rand((40, 1, 8), 20)
+    W = 5
+    k2, v2 = k.copy(), v.copy()
+    k2[:32] = np.nan          # rows sit at 36..39, so keys below 32 are never visible
+    v2[:32] = np.nan
+    assert np.array_equal(ora.attend(q, k2, v2, 0.3, window=W), ora.attend(q, k, v, 0.3, window=W))
+    assert np.array_equal(ora.attend_rows(q, k2, v2, 0.3, window=W), ora.attend_rows(q, k, v, 0.3, window=W))
