@@ -75,7 +75,17 @@ Readings where the pages are silent or ambiguous (also listed in the design doc):
   first block whose identity is already registered; a reused block that no
   request held counts against the free pages at admission; an allocation
   takes a page that holds no registered block when there is one, else the
-  most recently released registered block, whose registration ends.
+  most recently released registered block, whose registration ends;
+* sliding window (transformers, "Memory management": sliding layers keep a
+  fixed window of recent tokens by recycling a small set of pages, and do not
+  share blocks): at the start of a step, after finished requests are
+  released, every live request releases the pages that lie wholly below
+  ``cached - W + 1``, the lowest key any of its later rows can see; released
+  pages leave holes in its block table (the kernel never reads them); an
+  import allocates only the pages still inside its window; a request is
+  rejected as never fitting only if even its largest simultaneous need (its
+  window plus one chunk) exceeds the pool; a window together with block
+  sharing is invalid.
 
 Physical page ids are not unique (any free page is correct), so this model
 tracks page *counts* and block identities, not page ids.
@@ -89,6 +99,7 @@ import numpy as np
 
 WAITING, PREFILLING, DECODING, FINISHED = "waiting", "prefilling", "decoding", "finished"
 FIFO, PREFILL_FIRST = "fifo", "prefill_first"
+RELEASED = "released"        # a block-table entry whose page went back to the pool
 
 
 class SchedulerError(ValueError):
@@ -115,15 +126,22 @@ class Request:
     generated: int = 0
     state: str = WAITING
     tokens: Optional[tuple] = None
-    # one entry per held page: a Block when the page holds a registered block,
-    # else None (a page private to this request)
+    # one entry per logical page: a Block when the page holds a registered
+    # block, None for a page private to this request, RELEASED for a page
+    # below the sliding window that went back to the pool
     blocks: list = field(default_factory=list)
     registered: int = 0           # leading blocks that are registered or matched
     stop_registering: bool = False
+    released: int = 0             # leading entries that are RELEASED
 
     @property
     def pages(self) -> int:
+        """Length of the block table (logical pages)."""
         return len(self.blocks)
+
+    @property
+    def held(self) -> int:
+        return len(self.blocks) - self.released
 
 
 @dataclass
@@ -133,9 +151,10 @@ class ScheduledSeq:
     q_offset: int          # KV length before this step's tokens
     context_len: int       # KV length after this step's tokens
     is_decode: bool
-    pages: int             # pages the request holds after this step's allocation
-    blocks: tuple = ()     # per held page: the block's serial, or -1 if private
+    pages: int             # block-table length after this step's allocation
+    blocks: tuple = ()     # per logical page: block serial, -1 if private, -2 if released
     prefix_hit: int = 0    # tokens reused from shared blocks at admission
+    held: int = 0          # pages actually held (pages minus released ones)
 
 
 @dataclass
@@ -163,7 +182,7 @@ class Scheduler:
                  page_size: int = 16, max_prefill_chunk: int = 0, safety_margin: float = 0.0,
                  policy: str = FIFO, max_partial_prefills: int = 0,
                  max_long_partial_prefills: int = 0, long_prefill_threshold: int = 0,
-                 allow_block_sharing: bool = False):
+                 allow_block_sharing: bool = False, sliding_window: int = 0):
         if max_batch_tokens < 1 or max_requests_per_batch < 1 or num_pages < 1 or page_size < 1:
             raise SchedulerError("invalid", "budgets and pool size must be positive")
         if max_prefill_chunk < 0 or not (0.0 <= safety_margin < 1.0):
@@ -172,6 +191,8 @@ class Scheduler:
             raise SchedulerError("invalid", f"unknown policy {policy!r}")
         if min(max_partial_prefills, max_long_partial_prefills, long_prefill_threshold) < 0:
             raise SchedulerError("invalid", "prefill caps must be >= 0")
+        if sliding_window < 0 or (sliding_window > 0 and allow_block_sharing):
+            raise SchedulerError("invalid", "window must be >= 0 and excludes block sharing")
         self.max_batch_tokens = max_batch_tokens
         self.max_requests = max_requests_per_batch
         self.num_pages = num_pages
@@ -184,6 +205,7 @@ class Scheduler:
         self.max_long = max_long_partial_prefills
         self.long_threshold = long_prefill_threshold
         self.sharing = bool(allow_block_sharing)
+        self.window = sliding_window
         self.clean = num_pages            # free pages holding no registered block
         self.cached: list[Block] = []     # released registered blocks, newest last
         self.index: dict[tuple, Block] = {}
@@ -259,15 +281,23 @@ class Scheduler:
         final_kv = prompt_len + output_len - 1
         if tokens_cached >= final_kv and tokens_cached > 0:
             raise SchedulerError("invalid", "request has nothing left to do")
-        if _ceil_div(final_kv, self.page) > self.num_pages:
+        peak = _ceil_div(final_kv, self.page)
+        if self.window > 0:    # the window plus one chunk (+1 page for misalignment)
+            chunk = min(prompt_len, self.max_batch_tokens)
+            if self.chunk_cap > 0:
+                chunk = min(chunk, self.chunk_cap)
+            peak = min(peak, _ceil_div(self.window - 1 + chunk, self.page) + 1)
+        if peak > self.num_pages:
             raise SchedulerError("capacity", "request can never fit the page pool")
         r = Request(req_id, prompt_len, output_len, self._arrivals,
                     tokens=tuple(int(t) for t in tokens) if tokens is not None else None)
         if tokens_cached > 0:
-            need = _ceil_div(tokens_cached, self.page)
+            first = self._window_floor(tokens_cached)
+            need = _ceil_div(tokens_cached, self.page) - first
             if need > self.free:
                 raise SchedulerError("capacity", "not enough free pages to import")
-            r.blocks = [self._take() for _ in range(need)]
+            r.blocks = [RELEASED] * first + [self._take() for _ in range(need)]
+            r.released = first
             r.cached = tokens_cached
             if tokens_cached < prompt_len:
                 r.state = PREFILLING
@@ -282,6 +312,12 @@ class Scheduler:
         return sorted((r for r in self.requests.values() if r.state == state),
                       key=lambda r: r.arrival)
 
+    def _window_floor(self, cached: int) -> int:
+        """Logical pages wholly below every later row's window."""
+        if self.window <= 0:
+            return 0
+        return max(0, cached - self.window + 1) // self.page
+
     def _is_long(self, r) -> bool:
         return r.prompt_len > self.long_threshold
 
@@ -290,9 +326,17 @@ class Scheduler:
         # release what finished last step
         for r in self._ordered(FINISHED):
             for entry in r.blocks:
-                self._release(entry)
+                if entry is not RELEASED:
+                    self._release(entry)
             st.finished.append(r.req_id)
             del self.requests[r.req_id]
+        # pages that fell out of every live request's window
+        for r in sorted(self.requests.values(), key=lambda r: r.arrival):
+            lim = min(self._window_floor(r.cached), len(r.blocks))
+            while r.released < lim:
+                self._release(r.blocks[r.released])
+                r.blocks[r.released] = RELEASED
+                r.released += 1
 
         budget = {"tokens": self.max_batch_tokens, "slots": self.max_requests,
                   "prefills": 0, "long": 0}
@@ -338,11 +382,11 @@ class Scheduler:
                 chunk = min(r.prompt_len - r.cached, budget["tokens"])
                 if self.chunk_cap > 0:
                     chunk = min(chunk, self.chunk_cap)
-                chunk = min(chunk, (r.pages + self.free) * self.page - r.cached)
+                chunk = min(chunk, (len(r.blocks) + self.free) * self.page - r.cached)
                 if chunk <= 0:
                     st.stalled.append(r.req_id)
                     continue
-                need = _ceil_div(r.cached + chunk, self.page) - r.pages
+                need = _ceil_div(r.cached + chunk, self.page) - len(r.blocks)
                 for _ in range(need):
                     r.blocks.append(self._take())
                 st.new_pages += need
@@ -403,7 +447,8 @@ class Scheduler:
                 self._register(r)
             st.seqs.append(ScheduledSeq(
                 r.req_id, n, r.cached - n, r.cached, is_decode, r.pages,
-                tuple(b.serial if b is not None else -1 for b in r.blocks), hit))
+                tuple(-2 if b is RELEASED else (b.serial if b is not None else -1) for b in r.blocks),
+                hit, r.held))
         self.total_stalls += len(st.stalled)
         return st
 
@@ -417,6 +462,8 @@ class Scheduler:
         for r in self.requests.values():
             for i, e in enumerate(r.blocks):
                 fill = max(0, min(self.page, r.cached - i * self.page))
+                if e is RELEASED:
+                    continue
                 if e is None:
                     total += fill
                 else:

@@ -346,3 +346,76 @@ def test_sharing_pool_invariants_on_random_traces(seed):
         assert s.pages_in_use() == private + len(held)
         assert 0 <= s.clean and s.free <= s.num_pages
     assert s.prefix_hit_tokens > 0
+
+
+# --- sliding window: pages recycled below the window ----------------------------
+def test_window_releases_pages_below_every_later_row():
+    s = FifoScheduler(256, 8, 100, sliding_window=32)
+    s.submit(0, 100, 40)
+    st = s.step()                          # prefill 0..99: pages 0..6
+    assert (st.seqs[0].pages, st.seqs[0].held) == (7, 7)
+    st = s.step()                          # later rows see keys >= 100 - 31 = 69: pages 0..3 go
+    assert st.seqs[0].blocks[:4] == (-2, -2, -2, -2)
+    assert (st.seqs[0].pages, st.seqs[0].held, s.pages_in_use()) == (7, 3, 3)
+    # decodes at 100..111 stay in page 6; the decode at 112 adds page 7 and, its
+    # keys starting at 81, releases page 4 (64..79)
+    for _ in range(11):
+        s.step()
+    st = s.step()
+    assert (st.seqs[0].q_offset, st.seqs[0].pages, st.seqs[0].held, s.pages_in_use()) == (112, 8, 3, 3)
+    for _ in range(14):                    # decodes at 113..126
+        st = s.step()
+    assert st.seqs[0].q_offset == 126 and st.seqs[0].held == 3
+    st = s.step()                          # at 127 keys start at 96: page 5 (80..95) goes
+    assert (st.seqs[0].held, s.pages_in_use()) == (2, 2)
+    st = s.step()                          # at 128 a new page
+    assert (st.seqs[0].pages, st.seqs[0].held) == (9, 3)
+
+
+def test_window_lets_a_long_request_run_in_a_small_pool():
+    # 200 + 20 - 1 tokens need 14 pages; the pool has 8
+    with pytest.raises(SchedulerError) as e:
+        FifoScheduler(64, 8, 8).submit(0, 200, 20)
+    assert e.value.kind == "capacity"
+    s = FifoScheduler(64, 8, 8, max_prefill_chunk=64, sliding_window=32)
+    s.submit(0, 200, 20)                  # peak: ceil((31 + 64) / 16) + 1 = 7 pages
+    steps = _drive(s)
+    assert [x.seqs[0].q_len for x in steps[:4]] == [64, 64, 64, 8]
+    assert len(steps) == 4 + 19 and s.free == 8
+    assert max(x.seqs[0].held for x in steps) <= 7
+
+
+def test_window_import_allocates_only_the_window():
+    s = FifoScheduler(256, 8, 20, sliding_window=32)
+    s.submit(0, 100, 5, tokens_cached=100)   # keys from 69 on: pages 4, 5, 6
+    assert s.pages_in_use() == 3
+    st = s.step()
+    assert st.seqs[0].blocks[:4] == (-2, -2, -2, -2) and st.seqs[0].held == 3
+
+
+def test_window_excludes_block_sharing():
+    with pytest.raises(SchedulerError):
+        FifoScheduler(64, 8, 8, sliding_window=16, allow_block_sharing=True)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_window_pool_invariants_on_random_traces(seed):
+    rng = np.random.default_rng(300 + seed)
+    W = int(rng.choice([1, 16, 17, 40]))
+    s = FifoScheduler(80, 8, 40, max_prefill_chunk=int(rng.choice([0, 24])), sliding_window=W)
+    rid = 0
+    for _ in range(400):
+        if rng.random() < 0.4:
+            p = int(rng.integers(1, 300))
+            c = int(rng.integers(0, p + 20)) if rng.random() < 0.2 else 0
+            try:
+                s.submit(rid, p, int(rng.integers(1, 30)), tokens_cached=c)
+            except SchedulerError:
+                pass
+            rid += 1
+        st = s.step()
+        assert s.pages_in_use() == sum(r.held for r in s.requests.values())
+        for x in st.seqs:   # every page a row of this step can see is held
+            first_key = max(0, x.q_offset - W + 1)
+            assert all(b != -2 for b in x.blocks[first_key // 16:])
+    assert s.idle() or rid > 0
