@@ -157,14 +157,14 @@ POLICIES = {"fifo": CB_POLICY_FIFO, "prefill_first": CB_POLICY_PREFILL_FIRST}
 def builder_config(max_batch_tokens, max_requests_per_batch, num_pages, max_prefill_chunk=0,
                    safety_margin=0.0, page_shuffle_seed=0, policy="fifo", max_partial_prefills=0,
                    max_long_partial_prefills=0, long_prefill_threshold=0,
-                   allow_block_sharing=False) -> BuilderConfig:
+                   allow_block_sharing=False, sliding_window=0) -> BuilderConfig:
     """The builder's C configuration; argument meanings as in include/cb.h."""
     if policy not in POLICIES:
         raise ValueError(f"policy must be one of {sorted(POLICIES)}")
     return BuilderConfig(max_batch_tokens, max_requests_per_batch, num_pages, PAGE_SIZE,
                          max_prefill_chunk, safety_margin, page_shuffle_seed, POLICIES[policy],
                          max_partial_prefills, max_long_partial_prefills, long_prefill_threshold,
-                         1 if allow_block_sharing else 0)
+                         1 if allow_block_sharing else 0, sliding_window)
 
 
 class Builder:

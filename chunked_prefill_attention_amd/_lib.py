@@ -26,7 +26,7 @@ class BuilderConfig(C.Structure):
                 ("page_size", i32), ("max_prefill_chunk", i32), ("safety_margin", f32),
                 ("page_shuffle_seed", C.c_uint64), ("policy", i32), ("max_partial_prefills", i32),
                 ("max_long_partial_prefills", i32), ("long_prefill_threshold", i32),
-                ("allow_block_sharing", i32)]
+                ("allow_block_sharing", i32), ("sliding_window", i32)]
 
 
 class StepDesc(C.Structure):

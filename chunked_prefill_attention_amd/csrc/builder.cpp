@@ -45,6 +45,7 @@ struct Request {
   std::vector<int32_t> tokens;  // prompt tokens (empty: no sharing)
   int32_t registered = 0;       // leading blocks registered or matched
   bool stop_registering = false;
+  int32_t released = 0;         // leading block-table entries released (-1) below the window
 };
 
 uint64_t splitmix64(uint64_t& x) {
@@ -167,6 +168,13 @@ struct cb_builder {
   int32_t take_page() { return pool.take(); }
   int32_t free_pages() const { return pool.free(); }
 
+  // logical pages wholly below every later row's window, for a request with
+  // `cached` tokens in the cache
+  int32_t window_floor(int32_t cached) const {
+    if (cfg.sliding_window <= 0) return 0;
+    return std::max(0, cached - cfg.sliding_window + 1) / CB_PAGE_SIZE;
+  }
+
   // registered blocks matching r's prompt, stopping short of its last token
   void match(const Request& r, std::vector<int32_t>& out) const {
     out.clear();
@@ -227,6 +235,8 @@ int cb_builder_create(const cb_builder_config* config, cb_builder** out) {
     return cb::fail(CB_ERR_INVALID, "unknown scheduling policy %d", c.policy);
   if (c.max_partial_prefills < 0 || c.max_long_partial_prefills < 0 || c.long_prefill_threshold < 0)
     return cb::fail(CB_ERR_INVALID, "prefill caps and the long-prompt threshold must be >= 0");
+  if (c.sliding_window < 0 || (c.sliding_window > 0 && c.allow_block_sharing))
+    return cb::fail(CB_ERR_INVALID, "sliding_window must be >= 0 and cannot be combined with block sharing");
   cb_builder* b = new (std::nothrow) cb_builder();
   if (!b) return cb::fail(CB_ERR_INVALID, "out of host memory");
   b->cfg = c;
@@ -274,9 +284,15 @@ static int submit_impl(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_
   const int64_t final_kv = (int64_t)prompt_len + output_len - 1;
   if (tokens_cached > 0 && tokens_cached >= final_kv)
     return cb::fail(CB_ERR_INVALID, "request %lld has nothing left to do", (long long)req_id);
-  if (cb::ceil_div(final_kv, CB_PAGE_SIZE) > b->cfg.num_pages)
-    return cb::fail(CB_ERR_CAPACITY, "request %lld needs %lld pages; the pool has %d", (long long)req_id,
-                    (long long)cb::ceil_div(final_kv, CB_PAGE_SIZE), b->cfg.num_pages);
+  int64_t peak = cb::ceil_div(final_kv, CB_PAGE_SIZE);
+  if (b->cfg.sliding_window > 0) {  // the window plus one chunk, +1 page for alignment
+    int64_t chunk = std::min(prompt_len, b->cfg.max_batch_tokens);
+    if (b->cfg.max_prefill_chunk > 0) chunk = std::min<int64_t>(chunk, b->cfg.max_prefill_chunk);
+    peak = std::min(peak, cb::ceil_div((int64_t)b->cfg.sliding_window - 1 + chunk, CB_PAGE_SIZE) + 1);
+  }
+  if (peak > b->cfg.num_pages)
+    return cb::fail(CB_ERR_CAPACITY, "request %lld needs %lld pages at once; the pool has %d",
+                    (long long)req_id, (long long)peak, b->cfg.num_pages);
   auto r = std::make_unique<Request>();
   r->id = req_id;
   r->prompt_len = prompt_len;
@@ -284,10 +300,13 @@ static int submit_impl(cb_builder* b, int64_t req_id, int32_t prompt_len, int32_
   r->arrival = b->arrivals;
   if (tokens && b->pool.sharing) r->tokens.assign(tokens, tokens + prompt_len);
   if (tokens_cached > 0) {
-    int32_t need = (int32_t)cb::ceil_div(tokens_cached, CB_PAGE_SIZE);
+    const int32_t first = b->window_floor(tokens_cached);
+    int32_t need = (int32_t)cb::ceil_div(tokens_cached, CB_PAGE_SIZE) - first;
     if (need > b->free_pages())
       return cb::fail(CB_ERR_CAPACITY, "import of %lld needs %d pages; %d free", (long long)req_id, need,
                       b->free_pages());
+    r->pages.assign(first, -1);
+    r->released = first;
     for (int32_t i = 0; i < need; ++i) r->pages.push_back(b->take_page());
     r->cached = tokens_cached;
     if (tokens_cached < prompt_len) {
@@ -331,7 +350,8 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
     keep.reserve(b->reqs.size());
     for (auto& r : b->reqs) {
       if (r->state == State::Finished) {
-        for (int32_t p : r->pages) pool.release(p);
+        for (int32_t p : r->pages)
+          if (p >= 0) pool.release(p);
         b->o_finished.push_back(r->id);
         b->by_id.erase(r->id);
         b->total_finished++;
@@ -340,6 +360,17 @@ int cb_builder_step(cb_builder* b, cb_step* out) {
       }
     }
     b->reqs.swap(keep);
+  }
+  // pages that fell out of every live request's window
+  if (c.sliding_window > 0) {
+    for (auto& up : b->reqs) {
+      Request* r = up.get();
+      const int32_t lim = std::min<int32_t>(b->window_floor(r->cached), (int32_t)r->pages.size());
+      for (; r->released < lim; ++r->released) {
+        pool.release(r->pages[r->released]);
+        r->pages[r->released] = -1;
+      }
+    }
   }
 
   struct Pick { Request* r; int32_t n; bool decode; };
@@ -527,7 +558,10 @@ int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out) {
       case State::Decoding: out->num_decoding++; break;
       case State::Finished: out->num_finished_pending++; break;
     }
-    if (!b->pool.sharing) out->used_slots += r->cached;
+    if (!b->pool.sharing) {  // tokens in held pages
+      for (size_t i = (size_t)r->released; i < r->pages.size(); ++i)
+        out->used_slots += std::max(0, std::min<int32_t>(CB_PAGE_SIZE, r->cached - (int32_t)i * CB_PAGE_SIZE));
+    }
   }
   if (b->pool.sharing) {  // a shared page counts once, at its fill
     std::unordered_map<int32_t, int32_t> fill;

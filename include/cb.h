@@ -244,6 +244,15 @@ typedef struct {
    * tokens (cb_builder_submit_tokens) reuse registered full prompt blocks;
    * see cb_builder_submit_tokens. */
   int32_t allow_block_sharing;
+  /* [CBA] "Memory management": sliding-window layers keep only the most
+   * recent tokens and recycle their pages.  With sliding_window = W > 0 a
+   * query at position p sees keys p-W < j <= p (pass the same W to
+   * cb_attention_step); at the start of each step a request releases the
+   * pages wholly below cached - W + 1, leaving -1 in its block table; an
+   * import allocates only the pages inside its window; the "never fits"
+   * check uses the window plus one chunk.  Incompatible with
+   * allow_block_sharing (CB_ERR_INVALID).  0 = full attention. */
+  int32_t sliding_window;
 } cb_builder_config;
 
 /* The step descriptor.  Arrays are owned by the builder and stay valid until

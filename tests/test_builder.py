@@ -17,7 +17,7 @@ import workloads as wl
 
 
 POLICY_KEYS = ("policy", "max_partial_prefills", "max_long_partial_prefills", "long_prefill_threshold",
-               "allow_block_sharing")
+               "allow_block_sharing", "sliding_window")
 
 
 def _pair(**kw):
@@ -48,13 +48,18 @@ def _compare_step(so, sb, tables):
         row = sb.block_tables[s, :x.pages]
         assert (sb.block_tables[s, x.pages:] == 0).all()
         prev = tables.get(x.req_id)
-        if prev is not None:
-            assert np.array_equal(row[:len(prev)], prev)          # tables only grow
+        if prev is not None:   # tables only grow; an entry may only turn into a released hole
+            same = row[:len(prev)] == prev
+            assert (same | (row[:len(prev)] == -1)).all()
         tables[x.req_id] = row.copy()
         a, e = sb.query_start_loc[s], sb.query_start_loc[s + 1]
         assert np.array_equal(sb.slot_mapping[a:e], paging.slots_for(row, x.q_offset, x.context_len))
         for i, pg in enumerate(row.tolist()):
             ser = x.blocks[i] if x.blocks else -1
+            if ser == -2:
+                assert pg == -1, "released page still in the table"
+                continue
+            assert pg >= 0
             if ser < 0:
                 assert pg not in held, "private page held twice"
                 held[pg] = x.req_id
@@ -212,3 +217,42 @@ def test_policies_caps_and_sharing_match_oracle(seed):
     assert b.stats()["total_stalls"] == o.total_stalls
     if kw["allow_block_sharing"]:
         assert o.prefix_hit_tokens > 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sliding_window_traces_match_oracle(seed):
+    rng = np.random.default_rng(900 + seed)
+    kw = dict(max_batch_tokens=int(rng.integers(16, 200)), max_requests=int(rng.integers(1, 10)),
+              num_pages=int(rng.integers(12, 80)), chunk=int(rng.choice([0, 0, 16, 40])),
+              margin=float(rng.choice([0.0, 0.15])), shuffle=seed,
+              policy=str(rng.choice(["fifo", "prefill_first"])),
+              sliding_window=int(rng.choice([1, 15, 16, 17, 64, 200])))
+    o, b = _pair(**kw)
+    tables = {}
+    nid = 0
+    for step in range(400):
+        for _ in range(int(rng.poisson(0.6))):
+            p, q = int(rng.integers(1, 400)), int(rng.integers(1, 60))
+            cached = int(rng.integers(0, p + q - 1)) if rng.random() < 0.25 else 0
+            err_o = err_b = None
+            try:
+                o.submit(nid, p, q, cached)
+            except SchedulerError as e:
+                err_o = e.kind
+            try:
+                b.submit(nid, p, q, cached)
+            except cb.CbError as e:
+                err_b = {-1: "invalid", -5: "capacity"}[e.status]
+            assert err_o == err_b
+            nid += 1
+        so, sb = o.step(), b.step()
+        _compare_step(so, sb, tables)
+        st = b.stats()
+        assert st["free_pages"] == o.free
+        assert st["used_slots"] == o.used_slots()
+    assert b.stats()["total_stalls"] == o.total_stalls
+
+
+def test_window_and_sharing_together_are_rejected():
+    with pytest.raises(cb.CbError):
+        cb.Builder(64, 8, 100, sliding_window=16, allow_block_sharing=True)
