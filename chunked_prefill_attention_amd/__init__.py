@@ -84,12 +84,13 @@ def attention_workspace_bytes(num_seqs, num_decodes, num_tokens, num_q_heads, nu
 
 def attention_step(q, k_cache, v_cache, block_tables, query_start_loc, context_lens, q_offsets,
                    num_decodes: int, max_context_len: int, scale: float, out=None, workspace=None,
-                   stream=None):
+                   stream=None, sliding_window: int = 0):
     """Causal attention of every query row ``q[T, Hq, D]`` over its sequence's pages.
 
     ``block_tables[B, stride]``, ``query_start_loc[B+1]``, ``context_lens[B]``,
     ``q_offsets[B]`` are int32 device tensors.  Returns ``out[T, Hq, D]``.
     ``workspace`` (uint8 device tensor) is allocated here when not given.
+    ``sliding_window`` > 0 limits row ``p`` to keys ``p - W < j <= p``.
     """
     torch = _torch()
     T, hq, d = q.shape
@@ -116,7 +117,8 @@ def attention_step(q, k_cache, v_cache, block_tables, query_start_loc, context_l
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(query_start_loc, "query_start_loc", torch.int32), _dev(context_lens, "context_lens", torch.int32),
         _dev(q_offsets, "q_offsets", torch.int32), B, num_decodes, T, max_context_len, hq, hkv, d,
-        PAGE_SIZE, P, float(scale), dt, _dev(out, "out"), ws_ptr, ws_bytes, _stream(stream)))
+        PAGE_SIZE, P, float(scale), int(sliding_window), dt, _dev(out, "out"), ws_ptr, ws_bytes,
+        _stream(stream)))
     return out
 
 

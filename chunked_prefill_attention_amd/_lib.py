@@ -61,7 +61,7 @@ SIGNATURES = {
     "cb_kv_append": (C.c_int, [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
     "cb_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32, i32]),
     "cb_attention_step": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                    i32, i32, f32, i32, vp, vp, sz, vp]),
+                                    i32, i32, f32, i32, i32, vp, vp, sz, vp]),
     "cb_builder_create": (C.c_int, [C.POINTER(BuilderConfig), C.POINTER(vp)]),
     "cb_builder_clone": (C.c_int, [vp, C.POINTER(vp)]),
     "cb_builder_destroy": (None, [vp]),

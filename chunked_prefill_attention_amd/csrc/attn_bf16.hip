@@ -113,6 +113,7 @@ struct Params {
   int32_t pf_blocks;     // grid blocks reserved for prefill items
   int32_t dec_cap, pf_tile_cap, pf_item_cap;
   int32_t comb_dec_blocks;
+  int32_t window;        // sliding window in tokens; 0 = none
   float scale_log2;      // softmax scale * log2(e)
 };
 
@@ -165,6 +166,10 @@ __device__ __forceinline__ float pair_sum16(float x) {
 // keep the first n (0..2*words) 16-bit elements of a little-endian word
 __device__ __forceinline__ uint32_t keep16(uint32_t w, int first_elem, int n) {
   return (first_elem + 1 < n) ? w : (first_elem < n ? (w & 0xFFFFu) : 0u);
+}
+// drop the first n 16-bit elements (zero them), keep the rest
+__device__ __forceinline__ uint32_t drop16(uint32_t w, int first_elem, int n) {
+  return (first_elem >= n) ? w : (first_elem + 1 >= n ? (w & 0xFFFF0000u) : 0u);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -235,9 +240,36 @@ __device__ int block_exclusive_scan(int v, int* sh, int& total) {
 }
 
 // keys a prefill row tile needs: up to the last row's position (and the context)
-__device__ __forceinline__ int tile_key_end(int tile, int L, int G, int ctx, int off) {
-  const int last_row = min(tile * PF_ROWS + PF_ROWS, L * G) - 1;
-  return min(ctx, off + last_row / G + 1);
+__host__ __device__ __forceinline__ int tile_key_end(int tile, int L, int G, int ctx, int off) {
+  const int rows = L * G;
+  const int last_row = (tile * PF_ROWS + PF_ROWS < rows ? tile * PF_ROWS + PF_ROWS : rows) - 1;
+  const int e = off + last_row / G + 1;
+  return e < ctx ? e : ctx;
+}
+
+// Sliding window (transformers, "Continuous batching architecture", Memory
+// management): a row at position p sees keys p-window < j <= p.
+// The first key a row at `pos` sees.
+__host__ __device__ __forceinline__ int window_first_key(int pos, int window) {
+  return window > 0 && pos - window + 1 > 0 ? pos - window + 1 : 0;
+}
+// A decode row sits at ctx-1: the first page it reads.
+__host__ __device__ __forceinline__ int decode_first_page(int ctx, int window) {
+  return window_first_key(ctx - 1, window) >> 4;
+}
+// Pages a decode row reads, and its number of split items.
+__host__ __device__ __forceinline__ int decode_pages(int ctx, int window) {
+  return ctx > 0 ? ((ctx + 15) >> 4) - decode_first_page(ctx, window) : 0;
+}
+// The first key of a prefill row tile (its first row's window start), rounded
+// down to a key tile: where the tile's key splits begin.
+__host__ __device__ __forceinline__ int tile_key_base(int tile, int G, int off, int window) {
+  return window_first_key(off + tile * PF_ROWS / G, window) / PF_KEYS * PF_KEYS;
+}
+// Key splits of a prefill row tile.
+__host__ __device__ __forceinline__ int tile_splits(int tile, int L, int G, int ctx, int off, int window,
+                                                    int split_keys) {
+  return (tile_key_end(tile, L, G, ctx, off) - tile_key_base(tile, G, off, window) + split_keys - 1) / split_keys;
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
@@ -257,7 +289,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     if (s < p.num_decodes) {
       ctx = p.ctx_lens[s];
       t = p.qsl[s];
-      const int np = ctx > 0 ? (ctx + 15) >> 4 : 0;
+      const int np = decode_pages(ctx, p.window);
       nfull = np / SP;
       rem = np - nfull * SP;
       if (rem > 0) atomicAdd(&bucket[SP - rem], 1);
@@ -278,7 +310,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     const int s = base + tid;
     if (s < p.num_decodes) {
       const int ctx = p.ctx_lens[s];
-      const int np = ctx > 0 ? (ctx + 15) >> 4 : 0;
+      const int np = decode_pages(ctx, p.window);
       const int nfull = np / SP, rem = np - nfull * SP;
       int idx = -1;
       if (rem > 0) {
@@ -303,8 +335,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
       ctx = p.ctx_lens[s];
       off = p.q_off[s];
       ntiles = L > 0 ? (L * p.G + PF_ROWS - 1) / PF_ROWS : 0;
-      for (int t = 0; t < ntiles; ++t)
-        nitems += (tile_key_end(t, L, p.G, ctx, off) + p.pf_split_keys - 1) / p.pf_split_keys;
+      for (int t = 0; t < ntiles; ++t) nitems += tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
     }
     int ttotal, itotal;
     const int tex = block_exclusive_scan(ntiles, sh, ttotal) + tcarry;
@@ -312,7 +343,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     int it = iex;
     for (int k = 0; k < ntiles; ++k) {
       const int t = ntiles - 1 - k;
-      const int ns = (tile_key_end(t, L, p.G, ctx, off) + p.pf_split_keys - 1) / p.pf_split_keys;
+      const int ns = tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
       if (tex + k < p.pf_tile_cap) p.pf_tiles[tex + k] = make_int4(s, t, it, ns);
       for (int ks = 0; ks < ns; ++ks, ++it)
         if (it < p.pf_item_cap) p.pf_items[it] = make_int4(s, t, ks, ns);
@@ -362,8 +393,9 @@ __device__ __forceinline__ void decode_issue(DecodeBuf<D>& B, const Params& p, i
   for (int t = 0; t < D / 16; ++t) B.v[t] = stream_load(reinterpret_cast<const uint2*>(vb + voff + 256 * t));
 }
 
-template <int D>
-__device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx, int g,
+// WIN: a sliding window is set (the full-attention instance carries none of its code)
+template <int D, bool WIN>
+__device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx, int lo, int g,
                                                const bf16x8 (&qf)[D / 32], floatx4 (&o)[D / 16],
                                                float& m, float& l, float c) {
   floatx4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -380,6 +412,16 @@ __device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx,
     for (int t = 0; t < D / 16; ++t) {
       B.v[t].x = keep16(B.v[t].x, 0, n);
       B.v[t].y = keep16(B.v[t].y, 2, n);
+    }
+  }
+  if (WIN && pg * 16 < lo) {  // the page that holds the window start
+    const int n = lo - (pg * 16 + 4 * g);  // keys below the window among this lane's 4
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (r < n) ? -INFINITY : x[r];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      B.v[t].x = drop16(B.v[t].x, 0, n);
+      B.v[t].y = drop16(B.v[t].y, 2, n);
     }
   }
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -402,7 +444,7 @@ __device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx,
     o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(B.v[t]), as_short4(pk), o[t], 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int kvh = w % p.hkv;
   const int j = w / p.hkv;
@@ -418,9 +460,10 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int hl = lane & 15, g = lane >> 4;
   const int G = p.G;
   const int npages = (ctx + 15) >> 4;
-  const int pg0 = split * p.split_pages;
+  const int lo = WIN ? window_first_key(ctx - 1, p.window) : 0;  // first key in the window
+  const int pg0 = (lo >> 4) + split * p.split_pages;
   const int pg1 = min(pg0 + p.split_pages, npages);
-  const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
+  const int nsplit = ((WIN ? decode_pages(ctx, p.window) : npages) + p.split_pages - 1) / p.split_pages;
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
   // per-lane element offsets inside a (page, head) slab: K row hl, dims 8g + 32c;
   // V dim rows 16t + hl, keys 4g..4g+3
@@ -461,7 +504,7 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
       // readlane's lane index wraps past 63; the page is then unused (nxt >= pg1)
       const int phys = nxt < pg1 ? __builtin_amdgcn_readlane(my_page, (nxt - pg0) & 63) : -1;
       decode_issue<D>(buf[(r + PF) % NB], p, phys, kvh, koff, voff);
-      if (cur < pg1) decode_compute<D>(buf[r], cur, ctx, g, qf, o, m, l, c);
+      if (cur < pg1) decode_compute<D, WIN>(buf[r], cur, ctx, lo, g, qf, o, m, l, c);
     }
   }
 
@@ -520,10 +563,12 @@ __device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const 
   }
 }
 
-// Stage tile kt in LDS; V tokens at or past the context end are zeroed here,
-// where the loaded data is consumed anyway.
-template <int D>
-__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, int kt, int ctx, int tid) {
+// Stage tile kt in LDS; V tokens at or past the context end, and below the
+// row tile's first key (`kfloor`: pages there may have been released), are
+// zeroed here, where the loaded data is consumed anyway.
+template <int D, bool WIN>
+__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, int kt, int ctx, int kfloor,
+                                         int tid) {
   using Lds = PfLds<D>;
   uint8_t* kl = stage;
   uint8_t* vl = stage + Lds::K_BYTES;
@@ -536,19 +581,27 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
     const int dr = rem >> 1, hf = rem & 1;
     uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;
     uint4 vv = st.v[i];
-    const int n = ctx - ((kt * 4 + pgl) * 16 + hf * 8);  // valid tokens among these 8
+    const int k8 = (kt * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
+    const int n = ctx - k8;                          // valid tokens among these 8
     if (n < 8) {
       vv.x = keep16(vv.x, 0, n);
       vv.y = keep16(vv.y, 2, n);
       vv.z = keep16(vv.z, 4, n);
       vv.w = keep16(vv.w, 6, n);
     }
+    const int nlo = kfloor - k8;                     // tokens below the first key
+    if (WIN && nlo > 0) {
+      vv.x = drop16(vv.x, 0, nlo);
+      vv.y = drop16(vv.y, 2, nlo);
+      vv.z = drop16(vv.z, 4, nlo);
+      vv.w = drop16(vv.w, 6, nlo);
+    }
     *reinterpret_cast<uint2*>(dst) = make_uint2(vv.x, vv.y);
     *reinterpret_cast<uint2*>(dst + 8) = make_uint2(vv.z, vv.w);
   }
 }
 
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* smem) {
   using Lds = PfLds<D>;
   const int kvh = b % p.hkv;
@@ -574,16 +627,21 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const bool rvalid = row < R;
   const int qi = row / G;
   const int hh = row - qi * G;
-  const int kcap = min(off + qi, ctx - 1);  // last key this row may see
+  const int kcap = min(off + qi, ctx - 1);              // last key this row may see
+  const int W = WIN ? p.window : 0;
+  const int kfirst = window_first_key(off + qi, W);     // first key this row may see
 
-  // this item's key range, in whole 64-key tiles
-  const int k_lo = ks * p.pf_split_keys;
+  // this item's key range, in whole 64-key tiles, from the tile's first row's window
+  const int k_lo = (WIN ? tile_key_base(tile, G, off, W) : 0) + ks * p.pf_split_keys;
   const int k_hi = min(k_lo + p.pf_split_keys, tile_key_end(tile, L, G, ctx, off));
   const int kt0 = k_lo / PF_KEYS, kt1 = (k_hi + PF_KEYS - 1) / PF_KEYS;
+  const int kfloor = window_first_key(off + tile * PF_ROWS / G, W);  // no row of the tile sees below
   const int w_first_row = tile * PF_ROWS + wv * 32;
   const int w_last_row = min(w_first_row + 31, R - 1);
   const int w_kend = (w_first_row < R) ? min(ctx, off + w_last_row / G + 1) : 0;
-  const int w_kfull = min(ctx, off + w_first_row / G + 1);  // keys below are visible to every row
+  const int w_kfull = min(ctx, off + w_first_row / G + 1);  // keys below are visible to every row...
+  const int w_klo_min = window_first_key(off + w_first_row / G, W);  // ...and at or above the window
+  const int w_klo_max = window_first_key(off + w_last_row / G, W);  // of the wave's last row
 
   constexpr int NK = D / 16;  // QK k-steps of 16 dims
   constexpr int NO = D / 32;  // 32-dim output tiles
@@ -623,11 +681,11 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 
   uint8_t* stage0 = smem;
   uint8_t* stage1 = smem + Lds::STAGE;
-  if (kt0 < kt1) pf_store<D>(sa, stage0, kt0, ctx, tid);
+  if (kt0 < kt1) pf_store<D, WIN>(sa, stage0, kt0, ctx, kfloor, tid);
   __syncthreads();
   auto tile_step = [&](int kt, const uint8_t* cur) {
     const int kbase = kt * PF_KEYS;
-    if (kbase < w_kend) {
+    if (kbase < w_kend && (!WIN || kbase + PF_KEYS > w_klo_min)) {
       const uint8_t* kl = cur;
       const uint8_t* vl = cur + Lds::K_BYTES;
       // S^T = K Q^T for two 32-key subtiles: lane holds S^T[key 8(r/4)+4gg+r%4][row l32]
@@ -642,13 +700,14 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
           sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[cc], sc[sub], 0, 0, 0);
         }
       }
-      if (kbase + PF_KEYS > w_kfull) {  // straddles this wave's diagonal (or the context end)
+      // straddles this wave's diagonal (or the context end), or its window's lower edge
+      if (kbase + PF_KEYS > w_kfull || (WIN && kbase < w_klo_max)) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * gg + (r & 3);
-            sc[sub][r] = key <= kcap ? sc[sub][r] : -INFINITY;
+            sc[sub][r] = (key <= kcap && (!WIN || key >= kfirst)) ? sc[sub][r] : -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -702,12 +761,12 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   for (int kt = kt0; kt < kt1; kt += 2) {
     pf_fetch<D>(sa, p, pids, min(kt + 2, klast), kt0, ctx, kvh, tid);
     tile_step(kt, stage0);
-    pf_store<D>(sb, stage1, min(kt + 1, klast), ctx, tid);  // tile kt+1 (clamped)
+    pf_store<D, WIN>(sb, stage1, min(kt + 1, klast), ctx, kfloor, tid);  // tile kt+1 (clamped)
     __syncthreads();
     if (kt + 1 >= kt1) break;
     pf_fetch<D>(sb, p, pids, min(kt + 3, klast), kt0, ctx, kvh, tid);
     tile_step(kt + 1, stage1);
-    pf_store<D>(sa, stage0, min(kt + 2, klast), ctx, tid);  // tile kt+2 (clamped)
+    pf_store<D, WIN>(sa, stage0, min(kt + 2, klast), ctx, kfloor, tid);  // tile kt+2 (clamped)
     __syncthreads();
   }
 
@@ -742,19 +801,19 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 // four decode wavefronts each.  The no-prefill instantiation needs neither
 // LDS nor the prefill registers and runs at higher occupancy.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(256, 2) void attn_mixed_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
   if ((int)blockIdx.x < p.pf_blocks) {
-    prefill_tile<D>(p, blockIdx.x, smem);
+    prefill_tile<D, WIN>(p, blockIdx.x, smem);
     return;
   }
-  decode_wave<D>(p, ((int)blockIdx.x - p.pf_blocks) * 4 + (threadIdx.x >> 6));
+  decode_wave<D, WIN>(p, ((int)blockIdx.x - p.pf_blocks) * 4 + (threadIdx.x >> 6));
 }
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(CB_DEC_WG, CB_DEC_WAVES_PER_SIMD) void attn_decode_kernel(Params p) {
-  decode_wave<D>(p, (int)blockIdx.x * (CB_DEC_WG / 64) + (threadIdx.x >> 6));
+  decode_wave<D, WIN>(p, (int)blockIdx.x * (CB_DEC_WG / 64) + (threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -770,8 +829,7 @@ __device__ void combine_decode(const Params& p, int wave) {
   const int s = wave / p.hq, h = wave % p.hq;
   const int G = p.G, kvh = h / G, hl = h % G;
   const int ctx = p.ctx_lens[s];
-  const int npages = (ctx + 15) >> 4;
-  const int nsplit = (npages + p.split_pages - 1) / p.split_pages;
+  const int nsplit = (decode_pages(ctx, p.window) + p.split_pages - 1) / p.split_pages;
   if (nsplit <= 1) return;
   const int j0 = p.dec_first[s];
   const int jr = p.dec_rem[s];
@@ -904,6 +962,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.pf_tile_cap = (int32_t)pl.pf_tile_cap;
   p.pf_item_cap = (int32_t)pl.pf_item_cap;
   p.scale_log2 = a.scale * LOG2E;
+  p.window = a.window;
   const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
   const int64_t dec_blocks = (pl.dec_cap * a.hkv + 3) / 4;
   p.pf_blocks = (int32_t)pf_blocks;
@@ -922,11 +981,15 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   }
   if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
+  const bool win = a.window > 0;
   if (pf_blocks > 0) {
-    hipLaunchKernelGGL(attn_mixed_kernel<D>, dim3((unsigned)(pf_blocks + dec_blocks)), dim3(256), 0, stream, p);
+    const dim3 grid((unsigned)(pf_blocks + dec_blocks));
+    if (win) hipLaunchKernelGGL((attn_mixed_kernel<D, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((attn_mixed_kernel<D, false>), grid, dim3(256), 0, stream, p);
   } else if (dec_blocks > 0) {
-    const int64_t blocks = (pl.dec_cap * a.hkv + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64);
-    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3((unsigned)blocks), dim3(CB_DEC_WG), 0, stream, p);
+    const dim3 grid((unsigned)((pl.dec_cap * a.hkv + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64)));
+    if (win) hipLaunchKernelGGL((attn_decode_kernel<D, true>), grid, dim3(CB_DEC_WG), 0, stream, p);
+    else hipLaunchKernelGGL((attn_decode_kernel<D, false>), grid, dim3(CB_DEC_WG), 0, stream, p);
   }
   if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
   if (comb_dec + comb_pf > 0)
@@ -999,7 +1062,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
 // Mirrors plan_kernel: decode items longest first (every full split, then the
 // short last splits by decreasing length, sequences in order within a
 // length), prefill tiles heaviest (last) first with their key splits.
-void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G,
+void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G, int32_t window,
                       const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst) {
   const WorkListLayout L = work_list_layout(pl, num_decodes);
   uint8_t* base = static_cast<uint8_t*>(dst);
@@ -1012,7 +1075,7 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
   int64_t n = 0;
   int counts[65] = {0};
   for (int s = 0; s < num_decodes; ++s) {
-    const int np = ctx[s] > 0 ? (ctx[s] + 15) >> 4 : 0;
+    const int np = decode_pages(ctx[s], window);
     const int nfull = np / SP, rem = np - nfull * SP;
     first[s] = (int32_t)n;
     for (int k = 0; k < nfull && n < pl.dec_cap; ++k) dec[n++] = make_int4(s, k, ctx[s], qsl[s]);
@@ -1021,7 +1084,7 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
   int starts[65];
   for (int b = 0, acc = (int)n; b <= 64; ++b) { starts[b] = acc; acc += counts[b]; }
   for (int s = 0; s < num_decodes; ++s) {
-    const int np = ctx[s] > 0 ? (ctx[s] + 15) >> 4 : 0;
+    const int np = decode_pages(ctx[s], window);
     const int nfull = np / SP, rem = np - nfull * SP;
     rem_at[s] = -1;
     if (rem > 0) {
@@ -1038,9 +1101,7 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
     const int ntiles = Lq > 0 ? (Lq * G + PF_ROWS - 1) / PF_ROWS : 0;
     for (int k = 0; k < ntiles; ++k) {
       const int t = ntiles - 1 - k;
-      const int last_row = std::min(t * PF_ROWS + PF_ROWS, Lq * G) - 1;
-      const int kend = std::min(ctx[s], q_off[s] + last_row / G + 1);
-      const int ns = (kend + pl.pf_split_keys - 1) / pl.pf_split_keys;
+      const int ns = tile_splits(t, Lq, G, ctx[s], q_off[s], window, pl.pf_split_keys);
       if (nt < pl.pf_tile_cap) pft[nt] = make_int4(s, t, (int)ni, ns);
       ++nt;
       for (int ks = 0; ks < ns; ++ks, ++ni)

@@ -10,7 +10,9 @@
 // time, compute their scores from the block table, keep an online softmax
 // (running max and sum), and accumulate the weighted values with each lane
 // owning head_dim/64 output dimensions.  Only keys 0..min(p, ctx-1) are ever
-// read, so slots past the context never reach the arithmetic.
+// read (from p-window+1 on with a sliding window: transformers, "Continuous
+// batching architecture", Memory management), so slots outside never reach
+// the arithmetic.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int ctx = a.ctx_lens[s];
   const int pos = a.q_offsets[s] + (t - a.qsl[s]);
   const int nk = min(pos + 1, ctx);
+  const int k0 = a.window > 0 ? max(0, pos - a.window + 1) : 0;
 
   const float* __restrict__ qrow = static_cast<const float*>(a.q) + ((size_t)t * a.hq + h) * D;
   const float* __restrict__ kc = static_cast<const float*>(a.k_cache);
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 
-  for (int kb = 0; kb < nk; kb += 64) {
+  for (int kb = k0; kb < nk; kb += 64) {
     const int j = kb + lane;
     const bool valid = j < nk;
     int page = valid ? bt[j >> 4] : 0;

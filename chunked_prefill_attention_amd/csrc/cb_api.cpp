@@ -115,12 +115,12 @@ int cb_attention_step(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes,
                       int32_t num_tokens, int32_t max_context_len, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                      int32_t num_pages, float scale, int32_t dtype, void* out,
+                      int32_t num_pages, float scale, int32_t sliding_window, int32_t dtype, void* out,
                       void* workspace, size_t workspace_bytes, void* stream) {
   return cb::attention_step_impl(q, k_cache, v_cache, block_tables, block_table_stride, query_start_loc,
                                  context_lens, q_offsets, num_seqs, num_decodes, num_tokens, max_context_len,
-                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale, dtype, out,
-                                 workspace, workspace_bytes, stream, nullptr);
+                                 num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale,
+                                 sliding_window, dtype, out, workspace, workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"
@@ -131,8 +131,9 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
                         int32_t block_table_stride, const int32_t* query_start_loc, const int32_t* context_lens,
                         const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes, int32_t num_tokens,
                         int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t page_size, int32_t num_pages, float scale, int32_t dtype, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream, const WorkLists* lists) {
+                        int32_t page_size, int32_t num_pages, float scale, int32_t sliding_window,
+                        int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                        const WorkLists* lists) {
   cb::clear_error();
   if (int st = check_common(num_kv_heads, head_dim, page_size, num_pages, dtype)) return st;
   if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
@@ -148,6 +149,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
   if (num_tokens > 0 && num_seqs == 0)
     return cb::fail(CB_ERR_INVALID, "num_tokens > 0 with no sequences");
   if (!std::isfinite(scale)) return cb::fail(CB_ERR_INVALID, "scale must be finite");
+  if (sliding_window < 0) return cb::fail(CB_ERR_INVALID, "sliding_window must be >= 0");
   if ((int64_t)num_tokens * num_q_heads * head_dim >= (int64_t(1) << 40))
     return cb::fail(CB_ERR_INVALID, "step too large");
   if (num_tokens == 0) return CB_OK;
@@ -176,6 +178,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
   a.head_dim = head_dim;
   a.num_pages = num_pages;
   a.scale = scale;
+  a.window = sliding_window;
   a.out = out;
   a.workspace = workspace;
   const hipStream_t st = static_cast<hipStream_t>(stream);

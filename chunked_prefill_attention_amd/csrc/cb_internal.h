@@ -24,8 +24,9 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
                         int32_t block_table_stride, const int32_t* query_start_loc, const int32_t* context_lens,
                         const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes, int32_t num_tokens,
                         int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t page_size, int32_t num_pages, float scale, int32_t dtype, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream, const WorkLists* lists);
+                        int32_t page_size, int32_t num_pages, float scale, int32_t sliding_window,
+                        int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                        const WorkLists* lists);
 // Largest number of pages any live request of the builder holds.
 int32_t builder_max_pages_held(const cb_builder* b);
 // Deep copy of src's state into dst (dst keeps its address).

@@ -142,7 +142,8 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     const size_t at = (off + 3) & ~size_t(3);  // 16-byte aligned (int32 units)
     if ((int64_t)(at + lay.bytes / 4) <= e->slot_ints) {
       cb::build_work_lists(pl, d.num_seqs, d.num_decodes, e->cfg.num_q_heads / e->cfg.num_kv_heads,
-                           d.query_start_loc, d.context_lens, d.q_offsets, h + at);
+                           e->cfg.builder.sliding_window, d.query_start_loc, d.context_lens, d.q_offsets,
+                           h + at);
       const uint8_t* db = reinterpret_cast<const uint8_t*>(dv + at);
       e->lists.dec_items = db + lay.dec_items;
       e->lists.pf_items = db + lay.pf_items;
@@ -202,7 +203,8 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   st = cb::attention_step_impl(q, c.k_cache, c.v_cache, e->d_bt, d.block_table_stride, e->d_qsl, e->d_ctx,
                                e->d_off, d.num_seqs, d.num_decodes, d.num_tokens, d.max_context_len,
                                c.num_q_heads, c.num_kv_heads, c.head_dim, CB_PAGE_SIZE, c.builder.num_pages,
-                               c.scale, c.dtype, out, c.workspace, c.workspace_bytes, stream,
+                               c.scale, c.builder.sliding_window, c.dtype, out, c.workspace,
+                               c.workspace_bytes, stream,
                                e->have_lists ? &e->lists : nullptr);
   if (st == CB_OK) e->pending = false;
   return st;

@@ -28,6 +28,7 @@ struct AttnArgs {
   int32_t num_seqs, num_decodes, num_tokens, max_context_len;
   int32_t hq, hkv, head_dim, num_pages;
   float scale;
+  int32_t window;   // sliding window in tokens (keys p-window < j <= p); 0 = none
   void* out;
   void* workspace;
 };
@@ -69,7 +70,8 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes);
 // (laid out by work_list_layout) from the host copies of query_start_loc,
 // context_lens and q_offsets.
 void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t group,
-                      const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst);
+                      int32_t window, const int32_t* qsl, const int32_t* ctx, const int32_t* q_off,
+                      void* dst);
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t head_dim,

@@ -151,6 +151,12 @@ size_t cb_attention_workspace_bytes(int32_t num_seqs, int32_t num_decodes, int32
  *   max_context_len   host upper bound of context_lens (sizes the grid)
  *   Grouped-query mapping: query head h reads KV head h / (Hq / Hkv).
  *   scale             softmax scale (1/sqrt(head_dim) by convention)
+ *   sliding_window    0 for full causal attention; W > 0 restricts row p to
+ *                     keys p-W < j <= p ([CBA] "Memory management": sliding
+ *                     layers keep only a fixed window of recent tokens).  Block
+ *                     table entries for pages wholly below a sequence's first
+ *                     row's window are never read (they may be -1), and cache
+ *                     slots below a row's window do not affect it, NaN included
  *   workspace         device, >= cb_attention_workspace_bytes(...) bytes
  *                     (may be NULL when that is 0); contents on entry do not
  *                     matter; two calls that share a workspace must be
@@ -162,7 +168,7 @@ size_t cb_attention_workspace_bytes(int32_t num_seqs, int32_t num_decodes, int32
  * query_start_loc / context_lens / q_offsets relations above and
  * context_lens <= max_context_len.
  * Errors: CB_ERR_INVALID (null pointers, negative or inconsistent sizes,
- * Hq % Hkv != 0, stride < ceil(max_context_len/16)), CB_ERR_UNSUPPORTED
+ * sliding_window < 0, Hq % Hkv != 0, stride < ceil(max_context_len/16)), CB_ERR_UNSUPPORTED
  * (page_size != 16, head_dim not 64/128, group size Hq/Hkv > 16, dtype),
  * CB_ERR_WORKSPACE, CB_ERR_DEVICE.  num_tokens == 0 is a no-op.
  * ------------------------------------------------------------------------- */
@@ -172,8 +178,8 @@ int cb_attention_step(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes,
                       int32_t num_tokens, int32_t max_context_len, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                      int32_t num_pages, float scale, int32_t dtype, void* out,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      int32_t num_pages, float scale, int32_t sliding_window, int32_t dtype,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
  * cb_profile_events -- timing hook for the main attention kernel.

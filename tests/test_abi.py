@@ -39,13 +39,14 @@ FAKE = C.c_void_p(0x1000)  # never dereferenced: every case below fails validati
 
 def _step(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=64, qsl=FAKE, ctx=FAKE, off=FAKE, B=2, nd=1, T=5,
-             maxctx=1000, hq=8, hkv=2, d=128, page=16, pages=100, scale=0.088, dtype=1, out=FAKE,
+             maxctx=1000, hq=8, hkv=2, d=128, page=16, pages=100, scale=0.088, window=0, dtype=1, out=FAKE,
              ws=FAKE, wsb=0, stream=NULL)
     a.update(over)
     lib = _lib.load()
     return lib.cb_attention_step(a["q"], a["k"], a["v"], a["bt"], a["stride"], a["qsl"], a["ctx"], a["off"],
                                  a["B"], a["nd"], a["T"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["page"],
-                                 a["pages"], a["scale"], a["dtype"], a["out"], a["ws"], a["wsb"], a["stream"])
+                                 a["pages"], a["scale"], a["window"], a["dtype"], a["out"], a["ws"], a["wsb"],
+                                 a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -53,6 +54,7 @@ def _step(**over):
     (dict(hkv=0), -1), (dict(nd=3), -1), (dict(T=0, nd=1), -1), (dict(q=NULL), -1), (dict(out=NULL), -1),
     (dict(bt=NULL), -1), (dict(stride=10), -1), (dict(pages=0), -1), (dict(scale=float("nan")), -1),
     (dict(maxctx=0), -1), (dict(wsb=16), -3), (dict(ws=NULL, wsb=1 << 30), -3), (dict(B=0, T=3, nd=0), -1),
+    (dict(window=-1), -1),
 ])
 def test_attention_step_rejects_bad_arguments(over, status):
     assert _step(**over) == status

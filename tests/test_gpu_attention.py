@@ -6,6 +6,8 @@ single-query prefill rows, decodes with many splits, empty sequences,
 grouped-query sizes 1..16), bit-exact indexing probes, and invariances
 (physical page permutation, determinism, NaN in unused slots).
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -18,13 +20,14 @@ import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def _check_all(st: Step, out, what):
+def _check_all(st: Step, out, what, window=0):
     worst = 0.0
     for s, (c, n) in enumerate(st.seqs):
         if n == 0:
             continue
-        ref = ora.attend(st.q[s], st.k_hist[s], st.v_hist[s], st.scale)
-        am = ora.attend(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale) if st.dtype == "bf16" else None
+        ref = ora.attend(st.q[s], st.k_hist[s], st.v_hist[s], st.scale, window=window)
+        am = ora.attend(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale,
+                        window=window) if st.dtype == "bf16" else None
         worst = max(worst, compare(st.out_rows(out, s), ref, st.dtype, f"{what} seq {s} (ctx {c}, q {n})", am))
     return worst
 
@@ -50,13 +53,48 @@ CASES = {
 def test_step_matches_oracle(name, dtype):
     seqs, hq, hkv, d = CASES[name]
     say(f"step {name} {dtype}")
-    st = Step(seqs, hq, hkv, d, dtype, seed=hash(name) % 1000)
+    st = Step(seqs, hq, hkv, d, dtype, seed=zlib.crc32(name.encode()) % 1000)
     if name == "qlen1_in_prefill_set":
         st.num_decodes = 1            # later q_len == 1 rows go down the prefill path
     kc, vc = st.upload()
     out = st.run(kc, vc)
     worst = _check_all(st, out, name)
     say(f"  max abs err {worst:.2e}")
+
+
+WINDOW_CASES = [("decode_gqa4", 1), ("decode_gqa4", 100), ("decode_long_splits", 1000),
+                ("decode_long_splits", 16), ("prefill_only_gqa4", 100), ("prefill_only_gqa4", 1),
+                ("mixed_small", 17), ("mixed_small", 300), ("mixed_d64_g1", 64), ("mixed_g8", 1000),
+                ("mixed_g8", 130), ("g3_odd", 5), ("mixed_g16", 50), ("mixed_g2", 100000)]
+
+
+@pytest.mark.parametrize("name,window", WINDOW_CASES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("holes", [False, True])
+def test_sliding_window_matches_oracle(name, window, dtype, holes):
+    """Row p sees keys p-W < j <= p.  Pages wholly below a sequence's first
+    row's window are NaN-filled (and, with ``holes``, their block-table
+    entries become -1, as the builder leaves them): they must not matter."""
+    seqs, hq, hkv, d = CASES[name]
+    say(f"window {name} W={window} {dtype} holes={holes}")
+    st = Step(seqs, hq, hkv, d, dtype, seed=zlib.crc32(name.encode()) % 1000 + window)
+    kc, vc = st.upload()
+    bt = st.bt.copy()
+    dropped = 0
+    for s, (c, n) in enumerate(st.seqs):
+        first_key = max(0, c - n - window + 1)
+        for pg in range(first_key // 16):
+            kc[int(st.bt[s, pg])] = float("nan")
+            vc[int(st.bt[s, pg])] = float("nan")
+            if holes:
+                bt[s, pg] = -1
+            dropped += 1
+    q = to_dev(np.concatenate(st.q), dtype)
+    out = cb.attention_step(q, kc, vc, i32(bt), i32(st.qsl), i32(st.ctx), i32(st.off), st.num_decodes,
+                            st.max_ctx, st.scale, sliding_window=window)
+    torch.cuda.synchronize()
+    worst = _check_all(st, out, f"window {window}", window=window)
+    say(f"  {dropped} pages below the windows; max abs err {worst:.2e}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
