@@ -74,16 +74,24 @@ def counted_traffic(workload_name):
     return None
 
 
-def algorithmic(desc, hq, hkv, d, esize):
-    """Bytes the step must move and flops it must do (no padding, no re-reads)."""
+def algorithmic(desc, hq, hkv, d, esize, window=0):
+    """Bytes the step must move and flops it must do (no padding, no re-reads).
+
+    With a sliding window a sequence needs the keys from its first row's
+    window start on, and row p sees min(p + 1, window) keys."""
     import numpy as np
     ctx = desc.context_lens.astype(np.int64)
     ql = desc.q_lens.astype(np.int64)
     off = ctx - ql
-    kv = int((ctx * 2 * hkv * d * esize).sum())
+    first = np.maximum(0, off - window + 1) if window > 0 else np.zeros_like(off)
+    kv = int(((ctx - first) * 2 * hkv * d * esize).sum())
     qo = int(2 * desc.num_tokens * hq * d * esize)
-    meta = int((-(-ctx // 16)).sum() * 4 + (3 * desc.num_seqs + 1) * 4)
-    pairs = ql * off + ql * (ql + 1) // 2
+    meta = int((-(-ctx // 16) - first // 16).sum() * 4 + (3 * desc.num_seqs + 1) * 4)
+    if window > 0:
+        pairs = np.array([int(np.minimum(np.arange(o + 1, c + 1), window).sum()) for o, c in zip(off, ctx)],
+                         dtype=np.int64)
+    else:
+        pairs = ql * off + ql * (ql + 1) // 2
     flops = int((4 * d * hq * pairs).sum())
     return kv + qo + meta, flops, int(pairs.sum())
 
@@ -98,6 +106,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
     ap.add_argument("--page-order", default="shuffled", choices=["shuffled", "sequential"],
                     help="physical page ids: a seeded random permutation (default) or handed out in order")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -115,11 +125,14 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     w, advance = workload(args.workload)
+    if args.window > 0:
+        w.name += f"_window{args.window}"
     hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
     t_setup = time.perf_counter()
     layer = PagedAttentionLayer(hq, hkv, d, w.pool_pages, w.max_batch_tokens, w.max_requests, w.dtype,
                                 w.max_prefill_chunk, w.safety_margin,
-                                page_shuffle_seed=w.seed if args.page_order == "shuffled" else 0, device=dev)
+                                page_shuffle_seed=w.seed if args.page_order == "shuffled" else 0, device=dev,
+                                sliding_window=args.window)
     hist = {}
     for i, (p, o, c) in enumerate(w.requests):
         layer.builder.submit(i, p, o, c)
@@ -149,7 +162,7 @@ def main():
         f"{desc0.num_decodes} decodes, {T} query tokens, max ctx {desc0.max_context_len}")
 
     esize = 2 if w.dtype == "bf16" else 4
-    bytes_alg, flops_alg, pairs = algorithmic(desc0, hq, hkv, d, esize)
+    bytes_alg, flops_alg, pairs = algorithmic(desc0, hq, hkv, d, esize, args.window)
     lib = cb.load()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -189,7 +202,8 @@ def main():
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(flops_alg / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
     roof["traffic"] = counted_traffic(w.name)
-    roof["kernel"] = "attn_mixed_kernel<128>" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel<128>"
+    kname = "attn_mixed_kernel" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel"
+    roof["kernel"] = f"{kname}<{d}, {'true' if args.window > 0 else 'false'}>"   # the template instance timed
     roof["kernel_us"] = round(kern_s * 1e6, 2)
     roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
     log(f"[bench] host enqueue {(t_enq - t0) / args.steps * 1e3:.3f} ms/step")
@@ -198,7 +212,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(desc0, q, hist, hq, hkv, d, args.cpu_seconds, out)
+        cpu = cpu_baseline(desc0, q, hist, hq, hkv, d, args.cpu_seconds, out, args.window)
 
     rec = {
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "query tokens/s", "n_gpus": 1,
@@ -208,6 +222,7 @@ def main():
         "config": {"workload": w.name, "page_order": args.page_order, "num_seqs": desc0.num_seqs, "num_decodes": desc0.num_decodes,
                    "num_tokens": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "page_size": 16,
                    "max_batch_tokens": w.max_batch_tokens, "max_context_len": desc0.max_context_len,
+                   "sliding_window": args.window,
                    "kv_bytes_read": bytes_alg, "visible_pairs": pairs, "flops": flops_alg},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -215,7 +230,7 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(desc, q, hist, hq, hkv, d, budget_s, gpu_out):
+def cpu_baseline(desc, q, hist, hq, hkv, d, budget_s, gpu_out, window=0):
     """Time the fp64 oracle on the step's sequences (test infrastructure)."""
     import numpy as np
     from oracle import attention as ora
@@ -240,7 +255,7 @@ def cpu_baseline(desc, q, hist, hq, hkv, d, budget_s, gpu_out):
     while True:
         t0 = time.perf_counter()
         for qq, kk, vv, a, e in seqs:
-            ref = ora.attend(qq, kk, vv, scale)
+            ref = ora.attend(qq, kk, vv, scale, window=window)
             if reps == 0:
                 worst = max(worst, float(np.abs(ref - gh[a:e]).max()))
         t_used += time.perf_counter() - t0
