@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
     ap.add_argument("--page-order", default="shuffled", choices=["shuffled", "sequential"],
                     help="physical page ids: a seeded random permutation (default) or handed out in order")
+    ap.add_argument("--graphs", default="",
+                    help="Q,KV padding intervals: replay each padded step shape from a recorded HIP graph")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
     args = ap.parse_args()
@@ -127,12 +129,13 @@ def main():
     w, advance = workload(args.workload)
     if args.window > 0:
         w.name += f"_window{args.window}"
+    gq, gkv = (int(x) for x in args.graphs.split(",")) if args.graphs else (0, 0)
     hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
     t_setup = time.perf_counter()
     layer = PagedAttentionLayer(hq, hkv, d, w.pool_pages, w.max_batch_tokens, w.max_requests, w.dtype,
                                 w.max_prefill_chunk, w.safety_margin,
                                 page_shuffle_seed=w.seed if args.page_order == "shuffled" else 0, device=dev,
-                                sliding_window=args.window)
+                                sliding_window=args.window, graph_q_interval=gq, graph_kv_interval=gkv)
     hist = {}
     for i, (p, o, c) in enumerate(w.requests):
         layer.builder.submit(i, p, o, c)
@@ -158,6 +161,12 @@ def main():
     out = torch.empty_like(q)
     layer.attend(q, kn, vn, out=out)               # sizes the workspace
     torch.cuda.synchronize()
+    if layer.graphs:                               # the step's inputs live in the static buffers
+        layer.static_q[:T].copy_(q)
+        layer.static_k[:T].copy_(kn)
+        layer.static_v[:T].copy_(vn)
+        q, kn, vn, out = layer.static_q, layer.static_k, layer.static_v, layer.static_out
+        torch.cuda.synchronize()
     log(f"[bench] {w.name}: setup {time.perf_counter() - t_setup:.1f}s; step: {desc0.num_seqs} seqs, "
         f"{desc0.num_decodes} decodes, {T} query tokens, max ctx {desc0.max_context_len}")
 
@@ -166,18 +175,29 @@ def main():
     lib = cb.load()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for e in starts + stops:
+    span0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    span1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for e in starts + stops + span0 + span1:
         e.record()
-    stream = torch.cuda.current_stream(dev)
+    stream = layer.graph_stream if layer.graphs else torch.cuda.current_stream(dev)
 
     def one_step(k=None):
         layer.load_builder(snapshot)                           # same starting state each time
         layer.schedule(stream=stream)                          # a1 + a2
+        if layer.graphs:                                       # events around the whole graph
+            if k is not None:
+                starts[k].record(stream)
+            layer._attend(q, kn, vn, out, stream)              # a3 .. a7, replayed
+            if k is not None:
+                stops[k].record(stream)
+            return
         if k is not None:
+            span0[k].record(stream)
             lib.cb_profile_events(starts[k].cuda_event, stops[k].cuda_event)
         layer.attend(q, kn, vn, out=out, stream=stream)        # a3 .. a7
         if k is not None:
             lib.cb_profile_events(None, None)
+            span1[k].record(stream)
 
     for i in range(args.warmup):
         one_step()
@@ -191,7 +211,11 @@ def main():
     step_s = (t1 - t0) / args.steps
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
     kern_s = float(np.mean(kern_ms)) / 1e3
-    assert torch.isfinite(out.float()).all(), "non-finite attention output"
+    if layer.graphs:      # the graph's events already span append .. combine
+        span_s = kern_s
+    else:
+        span_s = float(np.mean([s.elapsed_time(e) for s, e in zip(span0, span1)])) / 1e3
+    assert torch.isfinite(out[:T].float()).all(), "non-finite attention output"
 
     t_hbm, t_mfma = bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     if t_hbm >= t_mfma:
@@ -204,9 +228,15 @@ def main():
     roof["traffic"] = counted_traffic(w.name)
     kname = "attn_mixed_kernel" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel"
     roof["kernel"] = f"{kname}<{d}, {'true' if args.window > 0 else 'false'}>"   # the template instance timed
+    if layer.graphs:
+        roof["kernel"] = "graph replay (kv_append + attention + combine)"
+        roof["traffic"] = None
+        roof["graphs"] = layer.graph_stats()
     roof["kernel_us"] = round(kern_s * 1e6, 2)
     roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
+    roof["device_span_us"] = round(span_s * 1e6, 2)   # kv_append .. combine on the device
     log(f"[bench] host enqueue {(t_enq - t0) / args.steps * 1e3:.3f} ms/step")
+    log(f"[bench] device span (append .. combine) {span_s * 1e6:.1f} us")
     log(f"[bench] step {step_s * 1e3:.3f} ms, attention kernel {kern_s * 1e6:.1f} us, "
         f"{bytes_alg / 1e9:.3f} GB algorithmic, {flops_alg / 1e9:.1f} GFLOP")
 
@@ -222,7 +252,7 @@ def main():
         "config": {"workload": w.name, "page_order": args.page_order, "num_seqs": desc0.num_seqs, "num_decodes": desc0.num_decodes,
                    "num_tokens": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "page_size": 16,
                    "max_batch_tokens": w.max_batch_tokens, "max_context_len": desc0.max_context_len,
-                   "sliding_window": args.window,
+                   "sliding_window": args.window, "graph_padding": [gq, gkv],
                    "kv_bytes_read": bytes_alg, "visible_pairs": pairs, "flops": flops_alg},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -79,6 +79,9 @@ SIGNATURES = {
     "cb_engine_attend": (C.c_int, [vp, vp, vp, vp, vp, vp]),
     "cb_engine_workspace_bytes": (sz, [vp]),
     "cb_engine_load_builder": (C.c_int, [vp, vp]),
+    "cb_engine_set_graphs": (C.c_int, [vp, i32, i32, i32]),
+    "cb_engine_padded_tokens": (i32, [vp]),
+    "cb_engine_graph_stats": (C.c_int, [vp, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]),
 }
 
 _lib = None

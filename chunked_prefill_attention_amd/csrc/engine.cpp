@@ -1,14 +1,38 @@
 // Native engine step: FIFO builder -> pinned staging -> one async upload ->
 // KV append -> attention, with no Python (or other host language) in the
 // per-step path.  Semantics in include/cb.h ("Engine").
+//
+// Graph replay (transformers, "Continuous batching architecture", CUDA
+// graphs): with padding intervals set, each step's metadata is laid out for a
+// padded shape (tokens rounded up to the q interval, the longest context to
+// the KV interval, decode and prefill sequence counts to multiples of 16 and
+// 4; padding sequences are empty and padding tokens have slot -1), so that
+// steps of one padded shape launch identical kernels with identical
+// arguments.  The append, attention and combine launches of a shape are
+// captured once into a HIP graph and replayed after that.
 #include <algorithm>
 #include <cstring>
+#include <map>
 #include <new>
+#include <tuple>
 
 #include <hip/hip_runtime_api.h>
 
 #include "cb_internal.h"
 #include "kernels.h"
+
+namespace {
+struct GraphKey {
+  int slot;
+  int32_t nseq, ndec, ntok, maxctx, stride;
+  const void *q, *k, *v, *out, *ws;
+  size_t ws_bytes;
+  auto tie() const { return std::tie(slot, nseq, ndec, ntok, maxctx, stride, q, k, v, out, ws, ws_bytes); }
+  bool operator<(const GraphKey& o) const { return tie() < o.tie(); }
+};
+constexpr size_t kMaxGraphs = 128;
+int32_t round_up(int32_t x, int32_t m) { return (int32_t)cb::ceil_div(x, m) * m; }
+}  // namespace
 
 struct cb_engine {
   cb_engine_config cfg{};
@@ -23,6 +47,17 @@ struct cb_engine {
   const int32_t *d_qsl = nullptr, *d_ctx = nullptr, *d_off = nullptr, *d_bt = nullptr, *d_slots = nullptr;
   bool have_lists = false;  // bf16: the step's work lists were built on the host
   cb::WorkLists lists{};
+  // the pending step as launched: the builder's sizes, or their padded shape
+  int32_t x_nseq = 0, x_ndec = 0, x_ntok = 0, x_maxctx = 0, x_stride = 0;
+  // graph replay
+  int32_t pad_q = 0, pad_kv = 0;  // 0: no padding
+  bool capture = false;
+  std::map<GraphKey, hipGraphExec_t> graphs;
+  int64_t n_captures = 0, n_replays = 0;
+  void drop_graphs() {
+    for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
+    graphs.clear();
+  }
 };
 
 extern "C" {
@@ -57,6 +92,7 @@ int cb_engine_create(const cb_engine_config* config, cb_engine** out) {
 
 void cb_engine_destroy(cb_engine* e) {
   if (!e) return;
+  e->drop_graphs();
   for (int i = 0; i < 2; ++i)
     if (e->copied[i]) {
       (void)hipEventSynchronize(e->copied[i]);
@@ -75,6 +111,7 @@ int cb_engine_set_metadata(cb_engine* e, int32_t* meta_device, int32_t* meta_hos
   if (slot_ints < 16) return cb::fail(CB_ERR_INVALID, "cb_engine_set_metadata: buffers too small");
   for (int i = 0; i < 2; ++i)
     if (e->slot_used[i]) (void)hipEventSynchronize(e->copied[i]);
+  e->drop_graphs();  // they read the old buffers
   e->cfg.meta_device = meta_device;
   e->cfg.meta_host = meta_host;
   e->cfg.meta_bytes = meta_bytes;
@@ -88,6 +125,7 @@ int cb_engine_set_metadata(cb_engine* e, int32_t* meta_device, int32_t* meta_hos
 int cb_engine_set_workspace(cb_engine* e, void* workspace, size_t workspace_bytes) {
   cb::clear_error();
   if (!e) return cb::fail(CB_ERR_INVALID, "cb_engine_set_workspace: null engine");
+  e->drop_graphs();
   e->cfg.workspace = workspace;
   e->cfg.workspace_bytes = workspace ? workspace_bytes : 0;
   return CB_OK;
@@ -98,12 +136,16 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   if (!e || !out) return cb::fail(CB_ERR_INVALID, "cb_engine_schedule: null argument");
   const cb_builder_config& bc = e->cfg.builder;
   // worst case of this step's metadata, before the builder changes state
-  const int64_t B = bc.max_requests_per_batch, T = bc.max_batch_tokens;
-  const int64_t stride = (int64_t)cb::builder_max_pages_held(e->builder) + cb::ceil_div(T, CB_PAGE_SIZE) + 1;
-  int64_t need = (B + 1) + 2 * B + B * std::min<int64_t>(stride, bc.num_pages) + T;
+  const bool pad = e->pad_q > 0;
+  const int64_t B = bc.max_requests_per_batch + (pad ? 18 : 0);
+  const int64_t T = bc.max_batch_tokens + (pad ? e->pad_q + 16 : 0);
+  const int64_t stride = (int64_t)cb::builder_max_pages_held(e->builder) + cb::ceil_div(T, CB_PAGE_SIZE) + 1 +
+                         (pad ? e->pad_kv / CB_PAGE_SIZE + 1 : 0);
+  const int64_t bt_pages = pad ? stride : std::min<int64_t>(stride, bc.num_pages);
+  int64_t need = (B + 1) + 2 * B + B * bt_pages + T;
   if (e->cfg.dtype == CB_BF16) {  // bound of the host-built work lists (int32 units)
     const int64_t G = e->cfg.num_q_heads / e->cfg.num_kv_heads;
-    const int64_t pages = std::min<int64_t>(stride, bc.num_pages);
+    const int64_t pages = bt_pages;
     const int64_t dec_cap = B * cb::ceil_div(pages, 8);
     const int64_t tiles = cb::ceil_div(T * G, 128) + B + 1;
     const int64_t items = tiles * (cb::ceil_div(pages * CB_PAGE_SIZE, 512) + 1);
@@ -128,22 +170,59 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     off += n;
     return at;
   };
-  const size_t o_qsl = put(d.query_start_loc, (size_t)d.num_seqs + 1);
-  const size_t o_ctx = put(d.context_lens, (size_t)d.num_seqs);
-  const size_t o_off = put(d.q_offsets, (size_t)d.num_seqs);
-  const size_t o_bt = put(d.block_tables, (size_t)d.num_seqs * d.block_table_stride);
-  const size_t o_sl = put(d.slot_mapping, (size_t)d.num_tokens);
+  size_t o_qsl, o_ctx, o_off, o_bt, o_sl;
+  if (!pad || d.num_tokens == 0) {
+    e->x_nseq = d.num_seqs;
+    e->x_ndec = d.num_decodes;
+    e->x_ntok = d.num_tokens;
+    e->x_maxctx = d.max_context_len;
+    e->x_stride = d.block_table_stride;
+    o_qsl = put(d.query_start_loc, (size_t)d.num_seqs + 1);
+    o_ctx = put(d.context_lens, (size_t)d.num_seqs);
+    o_off = put(d.q_offsets, (size_t)d.num_seqs);
+    o_bt = put(d.block_tables, (size_t)d.num_seqs * d.block_table_stride);
+    o_sl = put(d.slot_mapping, (size_t)d.num_tokens);
+  } else {
+    // padded shape: [decodes | empty | prefills | empty], tokens past the real
+    // ones belong to no sequence and are not written (slot -1)
+    const int32_t nd = d.num_decodes, np = d.num_seqs - d.num_decodes;
+    const int32_t nd_p = round_up(nd, 16), np_p = round_up(np, 4), B_p = nd_p + np_p;
+    e->x_nseq = B_p;
+    e->x_ndec = nd_p;
+    e->x_ntok = std::max(round_up(d.num_tokens, e->pad_q), nd_p);
+    e->x_maxctx = round_up(std::max(d.max_context_len, 1), e->pad_kv);
+    e->x_stride = e->x_maxctx / CB_PAGE_SIZE;
+    auto src_of = [&](int32_t s) { return s < nd ? s : (s >= nd_p && s < nd_p + np ? nd + (s - nd_p) : -1); };
+    o_qsl = off;
+    for (int32_t s = 0, last = 0; s < B_p; ++s) {
+      const int32_t r = src_of(s);
+      h[off++] = r >= 0 ? d.query_start_loc[r] : last;
+      last = r >= 0 ? d.query_start_loc[r + 1] : last;
+    }
+    h[off++] = d.num_tokens;
+    o_ctx = off;
+    for (int32_t s = 0; s < B_p; ++s) h[off++] = src_of(s) >= 0 ? d.context_lens[src_of(s)] : 0;
+    o_off = off;
+    for (int32_t s = 0; s < B_p; ++s) h[off++] = src_of(s) >= 0 ? d.q_offsets[src_of(s)] : 0;
+    o_bt = off;
+    for (int32_t s = 0; s < B_p; ++s) {
+      const int32_t r = src_of(s);
+      for (int32_t i = 0; i < e->x_stride; ++i)
+        h[off++] = (r >= 0 && i < d.block_table_stride) ? d.block_tables[(size_t)r * d.block_table_stride + i] : 0;
+    }
+    o_sl = put(d.slot_mapping, (size_t)d.num_tokens);
+    for (int32_t t = d.num_tokens; t < e->x_ntok; ++t) h[off++] = -1;
+  }
   e->have_lists = false;
-  if (e->cfg.dtype == CB_BF16 && d.num_tokens > 0) {
+  if (e->cfg.dtype == CB_BF16 && e->x_ntok > 0) {
     // the attention step's work lists, built here instead of by a device plan kernel
-    const cb::Bf16Plan pl = cb::plan_bf16(d.num_seqs, d.num_decodes, d.num_tokens, e->cfg.num_q_heads,
-                                          e->cfg.num_kv_heads, e->cfg.head_dim, std::max(d.max_context_len, 1));
-    const cb::WorkListLayout lay = cb::work_list_layout(pl, d.num_decodes);
+    const cb::Bf16Plan pl = cb::plan_bf16(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads,
+                                          e->cfg.num_kv_heads, e->cfg.head_dim, std::max(e->x_maxctx, 1));
+    const cb::WorkListLayout lay = cb::work_list_layout(pl, e->x_ndec);
     const size_t at = (off + 3) & ~size_t(3);  // 16-byte aligned (int32 units)
     if ((int64_t)(at + lay.bytes / 4) <= e->slot_ints) {
-      cb::build_work_lists(pl, d.num_seqs, d.num_decodes, e->cfg.num_q_heads / e->cfg.num_kv_heads,
-                           e->cfg.builder.sliding_window, d.query_start_loc, d.context_lens, d.q_offsets,
-                           h + at);
+      cb::build_work_lists(pl, e->x_nseq, e->x_ndec, e->cfg.num_q_heads / e->cfg.num_kv_heads,
+                           e->cfg.builder.sliding_window, h + o_qsl, h + o_ctx, h + o_off, h + at);
       const uint8_t* db = reinterpret_cast<const uint8_t*>(dv + at);
       e->lists.dec_items = db + lay.dec_items;
       e->lists.pf_items = db + lay.pf_items;
@@ -179,10 +258,37 @@ int cb_engine_load_builder(cb_engine* e, const cb_builder* src) {
 
 size_t cb_engine_workspace_bytes(const cb_engine* e) {
   if (!e || !e->pending) return 0;
-  const cb_step& d = e->step;
-  return cb_attention_workspace_bytes(d.num_seqs, d.num_decodes, d.num_tokens, e->cfg.num_q_heads,
-                                      e->cfg.num_kv_heads, e->cfg.head_dim, std::max(d.max_context_len, 1),
-                                      e->cfg.dtype);
+  return cb_attention_workspace_bytes(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads, e->cfg.num_kv_heads,
+                                      e->cfg.head_dim, std::max(e->x_maxctx, 1), e->cfg.dtype);
+}
+
+int32_t cb_engine_padded_tokens(const cb_engine* e) { return e && e->pending ? e->x_ntok : 0; }
+
+int cb_engine_set_graphs(cb_engine* e, int32_t q_padding_interval, int32_t kv_padding_interval,
+                         int32_t capture) {
+  cb::clear_error();
+  if (!e) return cb::fail(CB_ERR_INVALID, "cb_engine_set_graphs: null engine");
+  const bool off = q_padding_interval == 0 && kv_padding_interval == 0;
+  if (!off && (q_padding_interval < 1 || kv_padding_interval < CB_PAGE_SIZE ||
+               kv_padding_interval % CB_PAGE_SIZE != 0))
+    return cb::fail(CB_ERR_INVALID, "padding intervals: q >= 1 and kv a positive multiple of %d (or both 0)",
+                    CB_PAGE_SIZE);
+  if (off && capture) return cb::fail(CB_ERR_INVALID, "graph capture needs padding intervals");
+  e->drop_graphs();
+  e->pad_q = q_padding_interval;
+  e->pad_kv = kv_padding_interval;
+  e->capture = capture != 0;
+  e->pending = false;
+  return CB_OK;
+}
+
+int cb_engine_graph_stats(const cb_engine* e, int64_t* captures, int64_t* replays, int64_t* cached) {
+  cb::clear_error();
+  if (!e || !captures || !replays || !cached) return cb::fail(CB_ERR_INVALID, "cb_engine_graph_stats: null argument");
+  *captures = e->n_captures;
+  *replays = e->n_replays;
+  *cached = (int64_t)e->graphs.size();
+  return CB_OK;
 }
 
 int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void* v_new, void* out,
@@ -197,17 +303,51 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   if (need > 0 && (!c.workspace || c.workspace_bytes < need))
     return cb::fail(CB_ERR_WORKSPACE, "the scheduled step needs %zu bytes of workspace (have %zu)", need,
                     c.workspace_bytes);
-  int st = cb_kv_append(k_new, v_new, c.k_cache, c.v_cache, e->d_slots, d.num_tokens, c.num_kv_heads,
-                        c.head_dim, c.builder.num_pages, CB_PAGE_SIZE, c.dtype, stream);
-  if (st != CB_OK) return st;
-  st = cb::attention_step_impl(q, c.k_cache, c.v_cache, e->d_bt, d.block_table_stride, e->d_qsl, e->d_ctx,
-                               e->d_off, d.num_seqs, d.num_decodes, d.num_tokens, d.max_context_len,
-                               c.num_q_heads, c.num_kv_heads, c.head_dim, CB_PAGE_SIZE, c.builder.num_pages,
-                               c.scale, c.builder.sliding_window, c.dtype, out, c.workspace,
-                               c.workspace_bytes, stream,
-                               e->have_lists ? &e->lists : nullptr);
-  if (st == CB_OK) e->pending = false;
-  return st;
+  auto launch = [&]() {
+    int rc = cb_kv_append(k_new, v_new, c.k_cache, c.v_cache, e->d_slots, e->x_ntok, c.num_kv_heads,
+                          c.head_dim, c.builder.num_pages, CB_PAGE_SIZE, c.dtype, stream);
+    if (rc != CB_OK) return rc;
+    return cb::attention_step_impl(q, c.k_cache, c.v_cache, e->d_bt, e->x_stride, e->d_qsl, e->d_ctx, e->d_off,
+                                   e->x_nseq, e->x_ndec, e->x_ntok, e->x_maxctx, c.num_q_heads,
+                                   c.num_kv_heads, c.head_dim, CB_PAGE_SIZE, c.builder.num_pages, c.scale,
+                                   c.builder.sliding_window, c.dtype, out, c.workspace, c.workspace_bytes,
+                                   stream, e->have_lists ? &e->lists : nullptr);
+  };
+  if (!e->capture) {
+    const int st = launch();
+    if (st == CB_OK) e->pending = false;
+    return st;
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const GraphKey key{e->slot, e->x_nseq, e->x_ndec, e->x_ntok, e->x_maxctx, e->x_stride,
+                     q, k_new, v_new, out, c.workspace, c.workspace_bytes};
+  auto it = e->graphs.find(key);
+  if (it == e->graphs.end()) {
+    if (e->graphs.size() >= kMaxGraphs) e->drop_graphs();
+    cb::ProfileEventsOff quiet;  // no event records inside a captured graph
+    if (hipStreamBeginCapture(hs, hipStreamCaptureModeThreadLocal) != hipSuccess)
+      return cb::fail(CB_ERR_DEVICE, "cb_engine_attend: stream capture could not begin");
+    const int st = launch();
+    hipGraph_t graph = nullptr;
+    const hipError_t end = hipStreamEndCapture(hs, &graph);
+    if (st != CB_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st;
+    }
+    hipGraphExec_t exec = nullptr;
+    if (end != hipSuccess || !graph || hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return cb::fail(CB_ERR_DEVICE, "cb_engine_attend: graph capture failed");
+    }
+    (void)hipGraphDestroy(graph);
+    it = e->graphs.emplace(key, exec).first;
+    e->n_captures++;
+  }
+  if (hipGraphLaunch(it->second, hs) != hipSuccess)
+    return cb::fail(CB_ERR_DEVICE, "cb_engine_attend: graph launch failed");
+  e->n_replays++;
+  e->pending = false;
+  return CB_OK;
 }
 
 }  // extern "C"

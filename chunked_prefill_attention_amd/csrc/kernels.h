@@ -14,6 +14,12 @@ namespace cb {
 // null when profiling is off.  Per host thread.
 extern thread_local hipEvent_t g_prof_start;
 extern thread_local hipEvent_t g_prof_stop;
+// Suspends the profiling events of this thread for a scope (graph capture).
+struct ProfileEventsOff {
+  hipEvent_t start = g_prof_start, stop = g_prof_stop;
+  ProfileEventsOff() { g_prof_start = g_prof_stop = nullptr; }
+  ~ProfileEventsOff() { g_prof_start = start; g_prof_stop = stop; }
+};
 
 // Arguments of one attention step, already validated on the host.
 struct AttnArgs {

@@ -93,6 +93,7 @@ class PagedAttentionLayer:
                  max_batch_tokens: int, max_requests_per_batch: int, dtype: str = "bf16",
                  max_prefill_chunk: int = 0, safety_margin: float = 0.0, page_shuffle_seed: int = 0,
                  device=None, cache_fill: float = 0.0, meta_pages_per_request: int = 2048,
+                 graph_q_interval: int = 0, graph_kv_interval: int = 0, graph_capture: bool = True,
                  **policy_kw):
         import torch
         self.torch = torch
@@ -123,6 +124,16 @@ class PagedAttentionLayer:
         self.builder = Builder(0, 0, 0, _handle=self._lib.cb_engine_builder(h), _owned=False)
         self._desc = StepDesc()
         self._gen = 0
+        # graph replay: padded step shapes, static buffers, a capturable stream
+        self.graphs = graph_q_interval > 0 or graph_kv_interval > 0
+        if self.graphs:
+            check(self._lib.cb_engine_set_graphs(h, graph_q_interval, graph_kv_interval, int(graph_capture)))
+            rows = max_batch_tokens + max(graph_q_interval, 16)   # >= any padded token count
+            self.static_q = torch.zeros((rows, num_q_heads, head_dim), dtype=self.tdtype, device=self.device)
+            self.static_k = torch.zeros((rows, num_kv_heads, head_dim), dtype=self.tdtype, device=self.device)
+            self.static_v = torch.zeros_like(self.static_k)
+            self.static_out = torch.zeros_like(self.static_q)
+            self.graph_stream = torch.cuda.Stream(self.device)     # default priority
 
     def _alloc_meta(self, ints):
         torch = self.torch
@@ -137,8 +148,14 @@ class PagedAttentionLayer:
     __del__ = close
 
     def _stream(self, stream):
-        s = stream if stream is not None else self.torch.cuda.current_stream(self.device)
-        return C.c_void_p(s.cuda_stream)
+        if stream is None:
+            stream = self.graph_stream if self.graphs else self.torch.cuda.current_stream(self.device)
+        return C.c_void_p(stream.cuda_stream)
+
+    def graph_stats(self) -> dict:
+        c, r, n = C.c_int64(), C.c_int64(), C.c_int64()
+        check(self._lib.cb_engine_graph_stats(self._h, C.byref(c), C.byref(r), C.byref(n)))
+        return {"captures": c.value, "replays": r.value, "cached": n.value}
 
     # -- a1 + a2: builder step and metadata upload -----------------------------------------
     def schedule(self, stream=None) -> StepView:
@@ -159,12 +176,37 @@ class PagedAttentionLayer:
 
     # -- a3 .. a7: append + attention --------------------------------------------------------
     def attend(self, q, k_new, v_new, out=None, stream=None):
+        if self.graphs:
+            return self._attend_padded(q, k_new, v_new, out, stream)
         if out is None:
             out = self.torch.empty_like(q)
+        return self._attend(q, k_new, v_new, out, stream)
+
+    def _attend_padded(self, q, k_new, v_new, out, stream):
+        """Padded (graph) mode: the step runs on the static buffers, on the
+        layer's stream (or ``stream``), ordered after the caller's current stream."""
+        torch = self.torch
+        T = self._desc.num_tokens
+        cur = torch.cuda.current_stream(self.device)
+        for src, dst in ((q, self.static_q), (k_new, self.static_k), (v_new, self.static_v)):
+            if src.data_ptr() != dst.data_ptr():
+                dst[:T].copy_(src[:T])
+        gs = stream if stream is not None else self.graph_stream
+        gs.wait_stream(cur)
+        self._attend(self.static_q, self.static_k, self.static_v, self.static_out, gs)
+        cur.wait_stream(gs)
+        if out is None:
+            return self.static_out[:T]
+        out[:T].copy_(self.static_out[:T])
+        return out
+
+    def _attend(self, q, k_new, v_new, out, stream):
         args = (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), self._stream(stream))
         st = self._lib.cb_engine_attend(self._h, *args)
         if st == CB_ERR_WORKSPACE:
             need = self._lib.cb_engine_workspace_bytes(self._h)
+            # earlier steps (possibly on another stream) may still use the old one
+            self.torch.cuda.synchronize(self.device)
             self._ws = self.torch.empty(int(need * 1.25) + 256, dtype=self.torch.uint8, device=self.device)
             check(self._lib.cb_engine_set_workspace(self._h, self._ws.data_ptr(), self._ws.numel()))
             st = self._lib.cb_engine_attend(self._h, *args)

@@ -428,6 +428,41 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
  * cb_engine_builder stays valid. */
 int cb_engine_load_builder(cb_engine* e, const cb_builder* src);
 
+/* ----------------------------------------------------------------------------
+ * Graph replay.  [CBA] "CUDA graphs": the CPU cost of building and dispatching
+ * each step is removed by recording the step's GPU work once and replaying it
+ * for steps of matching shape; shapes change every step, so query lengths are
+ * padded to a multiple of a q interval and KV lengths to a multiple of a KV
+ * interval, and recorded graphs are kept per padded shape.
+ *
+ * With q_padding_interval >= 1 and kv_padding_interval a positive multiple of
+ * 16, cb_engine_schedule lays the step out for its padded shape: tokens
+ * rounded up to the q interval (padding tokens have slot -1 and belong to no
+ * sequence), the longest context rounded up to the KV interval (the block
+ * table stride follows), decode and prefill sequence counts rounded up to
+ * multiples of 16 and 4 (padding sequences are empty).  The descriptor
+ * returned to the caller is unchanged.  With capture != 0, cb_engine_attend
+ * records the append and attention launches of a new (padded shape, metadata
+ * slot, buffer addresses) key into a HIP graph and launches the graph; a
+ * later step with the same key replays it.  At most 128 graphs are kept (all
+ * are dropped when the limit is reached, and when the metadata buffers or the
+ * workspace are replaced).  capture == 0 pads without recording (the same
+ * kernels, launched directly).  (0, 0, 0) turns padding off.
+ *
+ * In padded mode q, k_new, v_new and out must hold cb_engine_padded_tokens()
+ * rows (rows past the step's tokens are read and written but mean nothing),
+ * and the stream must be capturable (not the legacy default stream).
+ * Errors: CB_ERR_INVALID (bad intervals, capture without padding). */
+int cb_engine_set_graphs(cb_engine* e, int32_t q_padding_interval, int32_t kv_padding_interval,
+                         int32_t capture);
+
+/* Rows the scheduled step's buffers must hold (its padded token count); 0
+ * without a scheduled step. */
+int32_t cb_engine_padded_tokens(const cb_engine* e);
+
+/* Graphs recorded and launched so far, and graphs held now. */
+int cb_engine_graph_stats(const cb_engine* e, int64_t* captures, int64_t* replays, int64_t* cached);
+
 /* Workspace the last scheduled step needs (0 if none). */
 size_t cb_engine_workspace_bytes(const cb_engine* e);
 
