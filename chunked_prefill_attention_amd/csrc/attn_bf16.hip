@@ -877,10 +877,16 @@ __device__ void combine_decode(const Params& p, int wave) {
   }
 }
 
+// One workgroup per (row tile, KV head, block of 16 rows): 16 threads per row,
+// each merging D/16 output dimensions over the tile's key splits.
+constexpr int CP_ROWS = 16;
 template <int D>
 __device__ void combine_prefill(const Params& p, int gb) {
-  const int kvh = gb % p.hkv;
-  const int tj = gb / p.hkv;
+  constexpr int E = D / 16;                 // dims per thread
+  const int rb = gb % (PF_ROWS / CP_ROWS);
+  const int tk = gb / (PF_ROWS / CP_ROWS);
+  const int kvh = tk % p.hkv;
+  const int tj = tk / p.hkv;
   if (tj >= p.pf_tile_cap) return;
   const int4 tr = p.pf_tiles[tj];
   if (tr.x < 0 || tr.w <= 1) return;
@@ -889,7 +895,8 @@ __device__ void combine_prefill(const Params& p, int gb) {
   const int G = p.G;
   const int t0 = p.qsl[s];
   const int R = (p.qsl[s + 1] - t0) * G;
-  const int rl = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int rl = rb * CP_ROWS + (threadIdx.x >> 4);   // row within the tile
+  const int dc = (threadIdx.x & 15) * E;               // first output dim
   const int row = tile * PF_ROWS + rl;
   if (row >= R) return;
   const float c = p.scale_log2;
@@ -897,23 +904,23 @@ __device__ void combine_prefill(const Params& p, int gb) {
   for (int i = 0; i < nsplit; ++i)
     M = fmaxf(M, p.pf_ml[((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl].x);
   float lsum = 0.f;
-  floatx4 acc[D / 8];
+  floatx4 acc[E / 4];
 #pragma unroll
-  for (int e = 0; e < D / 8; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < E / 4; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < nsplit; ++i) {
     const size_t prow = ((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl;
     const float2 ml = p.pf_ml[prow];
     const float w = ml.x == -INFINITY ? 0.f : fast_exp2((ml.x - M) * c);
     lsum = fmaf(w, ml.y, lsum);
-    const floatx4* po = reinterpret_cast<const floatx4*>(p.pf_o + prow * D + half * (D / 2));
+    const floatx4* po = reinterpret_cast<const floatx4*>(p.pf_o + prow * D + dc);
 #pragma unroll
-    for (int e = 0; e < D / 8; ++e) acc[e] += w * po[e];
+    for (int e = 0; e < E / 4; ++e) acc[e] += w * po[e];
   }
   const float inv = 1.f / lsum;
   const int qi = row / G, hh = row - qi * G;
-  uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + half * (D / 2);
+  uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + dc;
 #pragma unroll
-  for (int e = 0; e < D / 8; ++e) {
+  for (int e = 0; e < E / 4; ++e) {
     const uint2 v = make_uint2(pack_bf16x2(acc[e][0] * inv, acc[e][1] * inv),
                                pack_bf16x2(acc[e][2] * inv, acc[e][3] * inv));
     *reinterpret_cast<uint2*>(orow + 4 * e) = v;
@@ -968,7 +975,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.pf_blocks = (int32_t)pf_blocks;
   const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
   const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
-  const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv : 0;
+  const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv * (PF_ROWS / CP_ROWS) : 0;
   p.comb_dec_blocks = (int32_t)comb_dec;
 
   if (lists) {  // built by the caller: read them where they were uploaded

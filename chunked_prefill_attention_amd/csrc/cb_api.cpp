@@ -191,7 +191,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
   const cb::Bf16Plan plan = cb::plan_bf16(num_seqs, num_decodes, num_tokens, num_q_heads, num_kv_heads,
                                           head_dim, max_context_len);
   if (plan.dec_cap * num_kv_heads >= (int64_t(1) << 31) || plan.pf_item_cap * num_kv_heads >= (int64_t(1) << 30) ||
-      plan.pf_tile_cap * num_kv_heads >= (int64_t(1) << 30))
+      plan.pf_tile_cap * num_kv_heads >= (int64_t(1) << 27))   // the prefill combine runs 8 blocks per tile
     return cb::fail(CB_ERR_INVALID, "step too large for one launch");
   if (!workspace || workspace_bytes < plan.bytes)
     return cb::fail(CB_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu%s)", plan.bytes, workspace_bytes,
