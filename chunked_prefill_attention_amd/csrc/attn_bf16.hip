@@ -120,7 +120,7 @@ struct Params {
 template <int D>
 struct PfLds {
   static constexpr int KROW = D * 2 + 16;  // padded K row (bytes) in LDS
-  static constexpr int VROW = 40;          // padded (page, dim) row of 16 tokens (bytes)
+  static constexpr int VROW = 32;          // (page, dim) row of 16 tokens (bytes): 16-byte reads, no conflicts
   static constexpr int K_BYTES = PF_KEYS * KROW;
   static constexpr int V_BYTES = (PF_KEYS / 16) * D * VROW;
   static constexpr int STAGE = K_BYTES + V_BYTES;
@@ -579,7 +579,7 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
     const int r = rem / (D / 8), c16 = rem % (D / 8);
     *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = st.k[i];
     const int dr = rem >> 1, hf = rem & 1;
-    uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;
+    uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;  // tokens 8hf..8hf+7, natural order
     uint4 vv = st.v[i];
     const int k8 = (kt * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
     const int n = ctx - k8;                          // valid tokens among these 8
@@ -596,8 +596,7 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
       vv.z = drop16(vv.z, 4, nlo);
       vv.w = drop16(vv.w, 6, nlo);
     }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(vv.x, vv.y);
-    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(vv.z, vv.w);
+    *reinterpret_cast<uint4*>(dst) = vv;
   }
 }
 
@@ -736,23 +735,28 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
         }
       l += rs;
 
-      // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile)
+      // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile).
+      // The score tile leaves each lane keys 4gg..4gg+3 and 8+4gg..8+4gg+3 of
+      // a 16-key group; one swap of packed words between the lane halves
+      // gives lanes 0..31 keys 0..7 and lanes 32..63 keys 8..15, so each
+      // lane's V operand is one contiguous 16-byte read.
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int r0 = 8 * half;
-          const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
-                                      pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
-                                      pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
-                                      pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
+          uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
+                                pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
+                                pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
+                                pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
+          // v_permlane32_swap(a, b) exchanges a's lanes 32..63 with b's lanes 0..31
+          const auto sx = __builtin_amdgcn_permlane32_swap(pb.x, pb.z, false, false);
+          const auto sy = __builtin_amdgcn_permlane32_swap(pb.y, pb.w, false, false);
+          pb = make_uint4((uint32_t)sx[0], (uint32_t)sy[0], (uint32_t)sx[1], (uint32_t)sy[1]);
           const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
 #pragma unroll
           for (int dt = 0; dt < NO; ++dt) {
-            const uint8_t* vr = vpage + (32 * dt + l32) * Lds::VROW;
-            const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 8 * gg);
-            const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16 + 8 * gg);
-            const uint4 va = make_uint4(a0.x, a0.y, a1.x, a1.y);
+            const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + 16 * gg);
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
           }
         }
