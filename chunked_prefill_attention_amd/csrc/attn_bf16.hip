@@ -46,6 +46,7 @@
 // select and their V entries zeroed, so garbage or NaN there never reaches
 // the output.
 #include <hip/hip_runtime.h>
+#include <vector>
 
 #include <algorithm>
 #include <cmath>
@@ -96,7 +97,7 @@ struct Params {
   const int32_t* q_off;
   uint16_t* out;
   int4* dec_items;       // (sequence, split, context length, query row); sequence -1 = no work
-  int4* pf_items;        // (sequence, row tile, key split, number of splits); -1 = no work
+  int4* pf_items;        // (sequence, row tile, key split, partial slot); -1 = no work
   int4* pf_tiles;        // (sequence, row tile, first item, number of splits); -1 = none
   int32_t* dec_first;    // [num_decodes] first full-length decode item of each sequence
   int32_t* dec_rem;      // [num_decodes] the sequence's shorter last item, or -1
@@ -340,13 +341,29 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     int ttotal, itotal;
     const int tex = block_exclusive_scan(ntiles, sh, ttotal) + tcarry;
     const int iex = block_exclusive_scan(nitems, sh, itotal) + icarry;
-    int it = iex;
+    // tile records heaviest first, each with its block of partial slots;
+    // items split-major (every tile's split 0, then split 1, ...) so that
+    // workgroups running together read the same keys
+    int slot = iex, maxns = 0;
     for (int k = 0; k < ntiles; ++k) {
       const int t = ntiles - 1 - k;
       const int ns = tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
-      if (tex + k < p.pf_tile_cap) p.pf_tiles[tex + k] = make_int4(s, t, it, ns);
-      for (int ks = 0; ks < ns; ++ks, ++it)
-        if (it < p.pf_item_cap) p.pf_items[it] = make_int4(s, t, ks, ns);
+      if (tex + k < p.pf_tile_cap) p.pf_tiles[tex + k] = make_int4(s, t, slot, ns);
+      slot += ns;
+      maxns = max(maxns, ns);
+    }
+    int it = iex;
+    for (int ks = 0; ks < maxns; ++ks) {
+      int first = iex;
+      for (int k = 0; k < ntiles; ++k) {
+        const int t = ntiles - 1 - k;
+        const int ns = tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
+        if (ks < ns) {
+          if (it < p.pf_item_cap) p.pf_items[it] = make_int4(s, t, ks, first + ks);
+          ++it;
+        }
+        first += ns;
+      }
     }
     tcarry += ttotal;
     icarry += itotal;
@@ -611,16 +628,19 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   if (s < 0) return;
   const int tile = __builtin_amdgcn_readfirstlane(item.y);
   const int ks = __builtin_amdgcn_readfirstlane(item.z);
-  const int nsplit = __builtin_amdgcn_readfirstlane(item.w);
+  const int slot = __builtin_amdgcn_readfirstlane(item.w);  // where this split's partials go
   const int G = p.G;
   const int t0 = p.qsl[s];
   const int L = p.qsl[s + 1] - t0;
   const int ctx = p.ctx_lens[s];
   const int off = p.q_off[s];
+  const int nsplit = tile_splits(tile, L, G, ctx, off, WIN ? p.window : 0, p.pf_split_keys);
+  if (nsplit > 1 && slot >= p.pf_item_cap) return;  // work list overflowed (precondition broken)
   const int npages = (ctx + 15) >> 4;
   const int R = L * G;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, gg = lane >> 5;
+  const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // l32 with bits 2, 3 swapped
 
   const int row = tile * PF_ROWS + wv * 32 + l32;
   const bool rvalid = row < R;
@@ -656,19 +676,26 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   // in the second LDS stage and tile kt is computed.  Fetches past the last
   // tile re-read it (clamped), so every iteration issues the same loads and
   // the compiler never has to drain the one still in flight.
-  PfStage<D> sa, sb;
-  const int klast = kt1 - 1;
-  if (kt0 < kt1) {
-    pf_fetch<D>(sa, p, pids, kt0, kt0, ctx, kvh, tid);
-    pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), kt0, ctx, kvh, tid);
-  }
-
+  // the query fragment first: it is waited for once, here, while the first
+  // two K/V tiles stay in flight (a load still pending at the loop header
+  // would make the compiler wait inside the loop, draining the pipeline)
   bf16x8 qf[NK];
   {
     const uint16_t* qrow = p.q + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + 8 * gg;
 #pragma unroll
     for (int cc = 0; cc < NK; ++cc)
       qf[cc] = as_bf16x8(rvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
+  }
+  PfStage<D> sa, sb;
+  const int klast = kt1 - 1;
+  if (kt0 < kt1) {
+    pf_fetch<D>(sa, p, pids, kt0, kt0, ctx, kvh, tid);
+    pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), kt0, ctx, kvh, tid);
+  }
+#pragma unroll
+  for (int cc = 0; cc < NK; ++cc) {
+    const uint4 qq = __builtin_bit_cast(uint4, qf[cc]);
+    asm volatile("" ::"v"(qq.x), "v"(qq.y), "v"(qq.z), "v"(qq.w));
   }
   floatx16 o[NO];
 #pragma unroll
@@ -687,7 +714,10 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     if (kbase < w_kend && (!WIN || kbase + PF_KEYS > w_klo_min)) {
       const uint8_t* kl = cur;
       const uint8_t* vl = cur + Lds::K_BYTES;
-      // S^T = K Q^T for two 32-key subtiles: lane holds S^T[key 8(r/4)+4gg+r%4][row l32]
+      // S^T = K Q^T for two 32-key subtiles.  MFMA row m reads key krow(m)
+      // (bits 2 and 3 of m swapped), so that lane (l32, gg) receives, for
+      // r = 0..15, key 16(r/8) + 8gg + r%8 of its subtile: the 8 consecutive
+      // keys the P V product takes from it, with no exchange between lanes.
       floatx16 sc[2];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
@@ -695,7 +725,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
         for (int r = 0; r < 16; ++r) sc[sub][r] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < NK; ++cc) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + l32) * Lds::KROW + (16 * cc + 8 * gg) * 2);
+          const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + krow) * Lds::KROW + (16 * cc + 8 * gg) * 2);
           sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[cc], sc[sub], 0, 0, 0);
         }
       }
@@ -705,7 +735,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = kbase + sub * 32 + 8 * (r >> 2) + 4 * gg + (r & 3);
+            const int key = kbase + sub * 32 + 16 * (r >> 3) + 8 * gg + (r & 7);
             sc[sub][r] = (key <= kcap && (!WIN || key >= kfirst)) ? sc[sub][r] : -INFINITY;
           }
       }
@@ -735,24 +765,18 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
         }
       l += rs;
 
-      // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile).
-      // The score tile leaves each lane keys 4gg..4gg+3 and 8+4gg..8+4gg+3 of
-      // a 16-key group; one swap of packed words between the lane halves
-      // gives lanes 0..31 keys 0..7 and lanes 32..63 keys 8..15, so each
-      // lane's V operand is one contiguous 16-byte read.
+      // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile):
+      // lane (l32, gg) holds P for keys 8gg..8gg+7 of the page, and reads V
+      // for the same keys as one contiguous 16-byte load.
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int r0 = 8 * half;
-          uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
-                                pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
-                                pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
-                                pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
-          // v_permlane32_swap(a, b) exchanges a's lanes 32..63 with b's lanes 0..31
-          const auto sx = __builtin_amdgcn_permlane32_swap(pb.x, pb.z, false, false);
-          const auto sy = __builtin_amdgcn_permlane32_swap(pb.y, pb.w, false, false);
-          pb = make_uint4((uint32_t)sx[0], (uint32_t)sy[0], (uint32_t)sx[1], (uint32_t)sy[1]);
+          const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
+                                      pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
+                                      pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
+                                      pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
           const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
 #pragma unroll
           for (int dt = 0; dt < NO; ++dt) {
@@ -788,7 +812,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
         *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
       }
   } else {
-    const size_t prow = ((size_t)j * p.hkv + kvh) * PF_ROWS + wv * 32 + l32;
+    const size_t prow = ((size_t)slot * p.hkv + kvh) * PF_ROWS + wv * 32 + l32;
     float* po = p.pf_o + prow * D;
 #pragma unroll
     for (int dt = 0; dt < NO; ++dt)
@@ -1107,16 +1131,31 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
   }
   for (int64_t i = n; i < pl.dec_cap; ++i) dec[i] = make_int4(-1, 0, 0, 0);
   int64_t nt = 0, ni = 0;
+  std::vector<int> tns;
   for (int s = num_decodes; s < num_seqs; ++s) {
     const int Lq = qsl[s + 1] - qsl[s];
     const int ntiles = Lq > 0 ? (Lq * G + PF_ROWS - 1) / PF_ROWS : 0;
-    for (int k = 0; k < ntiles; ++k) {
+    tns.assign(ntiles, 0);
+    const int64_t base = ni;
+    int maxns = 0;
+    for (int k = 0; k < ntiles; ++k) {  // tile records heaviest first, slots per tile
       const int t = ntiles - 1 - k;
-      const int ns = tile_splits(t, Lq, G, ctx[s], q_off[s], window, pl.pf_split_keys);
-      if (nt < pl.pf_tile_cap) pft[nt] = make_int4(s, t, (int)ni, ns);
+      tns[k] = tile_splits(t, Lq, G, ctx[s], q_off[s], window, pl.pf_split_keys);
+      if (nt < pl.pf_tile_cap) pft[nt] = make_int4(s, t, (int)ni, tns[k]);
       ++nt;
-      for (int ks = 0; ks < ns; ++ks, ++ni)
-        if (ni < pl.pf_item_cap) pfi[ni] = make_int4(s, t, ks, ns);
+      ni += tns[k];
+      maxns = std::max(maxns, tns[k]);
+    }
+    int64_t it = base;
+    for (int ks = 0; ks < maxns; ++ks) {  // items split-major
+      int64_t first = base;
+      for (int k = 0; k < ntiles; ++k) {
+        if (ks < tns[k]) {
+          if (it < pl.pf_item_cap) pfi[it] = make_int4(s, ntiles - 1 - k, ks, (int)(first + ks));
+          ++it;
+        }
+        first += tns[k];
+      }
     }
   }
   for (int64_t i = nt; i < pl.pf_tile_cap; ++i) pft[i] = make_int4(-1, 0, 0, 0);

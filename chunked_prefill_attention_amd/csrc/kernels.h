@@ -60,7 +60,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
 // device plan kernel is skipped.
 struct WorkLists {
   const void* dec_items;     // int4 [dec_cap]: (sequence, split, context, query row); -1 = none
-  const void* pf_items;      // int4 [pf_item_cap]: (sequence, row tile, key split, splits)
+  const void* pf_items;      // int4 [pf_item_cap]: (sequence, row tile, key split, partial slot)
   const void* pf_tiles;      // int4 [pf_tile_cap]: (sequence, row tile, first item, splits)
   const int32_t* dec_first;  // [num_decodes]
   const int32_t* dec_rem;    // [num_decodes]
