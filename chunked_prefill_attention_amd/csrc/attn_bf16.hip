@@ -81,7 +81,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #define CB_RESCALE_SLACK 8.0f
 #endif
 
-constexpr int PF_ROWS = 128;  // query rows per prefill workgroup (4 waves x 32)
+#ifndef CB_PF_THREADS
+#define CB_PF_THREADS 256
+#endif
+constexpr int PF_THREADS = CB_PF_THREADS;   // threads of a prefill workgroup
+constexpr int PF_WAVES = PF_THREADS / 64;
+constexpr int PF_ROWS = PF_WAVES * 32;      // query rows per prefill workgroup (32 per wave)
 constexpr int PF_KEYS = 64;   // keys per prefill tile (4 pages)
 constexpr int PF_MAX_PAGES = 512;                          // page ids one prefill item stages in LDS
 constexpr int PF_MAX_KEYS = (PF_MAX_PAGES - 4) * 16 / PF_KEYS * PF_KEYS;  // largest key range per item
@@ -550,19 +555,20 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct PfStage {            // one thread's share of one 64-key K/V tile
-  uint4 k[D / 32];
-  uint4 v[D / 32];
+  static constexpr int N = 8 * D / PF_THREADS;  // 16-byte chunks of K (and of V) per thread
+  uint4 k[N];
+  uint4 v[N];
 };
 
 template <int D>
 __device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int* pids, int kt, int kt0,
                                          int ctx, int kvh, int tid) {
   // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens.
-  // Chunk i of a thread lies in page (tid + 256 i) / 2D of the tile, the same
-  // page for the whole wavefront; its id comes from LDS (-1 = no page).
+  // Chunk i of a thread lies in page (tid + PF_THREADS i) / 2D of the tile,
+  // the same page for the whole wavefront; its id comes from LDS (-1 = no page).
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < PfStage<D>::N; ++i) {
+    const int e = tid + PF_THREADS * i;
     const int pgl = e / (2 * D), rem = e % (2 * D);
     const int pg = kt * 4 + pgl;
     // pages past the context (id -1) read page 0; their keys are masked by
@@ -590,8 +596,8 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
   uint8_t* kl = stage;
   uint8_t* vl = stage + Lds::K_BYTES;
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int e = tid + 256 * i;
+  for (int i = 0; i < PfStage<D>::N; ++i) {
+    const int e = tid + PF_THREADS * i;
     const int pgl = e / (2 * D), rem = e % (2 * D);
     const int r = rem / (D / 8), c16 = rem % (D / 8);
     *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = st.k[i];
@@ -667,7 +673,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
   // the item's page ids, staged once (at most PF_MAX_PAGES; the host caps the key range)
   int* pids = reinterpret_cast<int*>(smem + Lds::BYTES);
-  for (int i = tid; i < (kt1 - kt0) * 4; i += 256) {
+  for (int i = tid; i < (kt1 - kt0) * 4; i += PF_THREADS) {
     const int pg = kt0 * 4 + i;
     pids[i] = pg < npages ? btrow[pg] : -1;
   }
@@ -830,13 +836,13 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 // LDS nor the prefill registers and runs at higher occupancy.
 // ---------------------------------------------------------------------------
 template <int D, bool WIN>
-__global__ __launch_bounds__(256, 2) void attn_mixed_kernel(Params p) {
+__global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
   if ((int)blockIdx.x < p.pf_blocks) {
     prefill_tile<D, WIN>(p, blockIdx.x, smem);
     return;
   }
-  decode_wave<D, WIN>(p, ((int)blockIdx.x - p.pf_blocks) * 4 + (threadIdx.x >> 6));
+  decode_wave<D, WIN>(p, ((int)blockIdx.x - p.pf_blocks) * PF_WAVES + (threadIdx.x >> 6));
 }
 
 template <int D, bool WIN>
@@ -999,7 +1005,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.scale_log2 = a.scale * LOG2E;
   p.window = a.window;
   const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
-  const int64_t dec_blocks = (pl.dec_cap * a.hkv + 3) / 4;
+  const int64_t dec_blocks = (pl.dec_cap * a.hkv + PF_WAVES - 1) / PF_WAVES;
   p.pf_blocks = (int32_t)pf_blocks;
   const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
   const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
@@ -1019,8 +1025,8 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   const bool win = a.window > 0;
   if (pf_blocks > 0) {
     const dim3 grid((unsigned)(pf_blocks + dec_blocks));
-    if (win) hipLaunchKernelGGL((attn_mixed_kernel<D, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((attn_mixed_kernel<D, false>), grid, dim3(256), 0, stream, p);
+    if (win) hipLaunchKernelGGL((attn_mixed_kernel<D, true>), grid, dim3(PF_THREADS), 0, stream, p);
+    else hipLaunchKernelGGL((attn_mixed_kernel<D, false>), grid, dim3(PF_THREADS), 0, stream, p);
   } else if (dec_blocks > 0) {
     const dim3 grid((unsigned)((pl.dec_cap * a.hkv + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64)));
     if (win) hipLaunchKernelGGL((attn_decode_kernel<D, true>), grid, dim3(CB_DEC_WG), 0, stream, p);
