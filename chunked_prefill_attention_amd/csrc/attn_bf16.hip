@@ -1045,11 +1045,13 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   Bf16Plan pl{};
   const int64_t max_pages = (max_context_len + 15) / 16;
   const int64_t G = hkv > 0 ? hq / hkv : 1;
-  // decode: pages per wavefront, so that the decode grid has >= 16k wavefronts
+  // decode: the longest split (pages per wavefront) that still gives the
+  // decode grid >= 8k wavefronts (about 2-3 rounds of the chip's wave slots);
+  // longer splits write fewer partials for the combine
   const int64_t lanes = (int64_t)num_decodes * hkv;
   pl.split_pages = 8;
   for (int sp : {64, 32, 16}) {
-    if (lanes * ((max_pages + sp - 1) / sp) >= 16384) { pl.split_pages = sp; break; }
+    if (lanes * ((max_pages + sp - 1) / sp) >= 8192) { pl.split_pages = sp; break; }
   }
   pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);
   // prefill: row tiles bound by the query tokens; key ranges cut so that about
