@@ -81,6 +81,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #define CB_RESCALE_SLACK 8.0f
 #endif
 
+#ifndef CB_PF_TARGET_ITEMS  // prefill key ranges are cut for about this many workgroups
+#define CB_PF_TARGET_ITEMS 1024
+#endif
+#ifndef CB_PF_MIN_KEYS      // ... but never shorter than this (a multiple of 64)
+#define CB_PF_MIN_KEYS 512
+#endif
 #ifndef CB_PF_THREADS
 #define CB_PF_THREADS 256
 #endif
@@ -1059,8 +1065,9 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t np = num_seqs - num_decodes;
   pl.pf_tile_cap = np > 0 ? ((int64_t)(num_tokens - num_decodes) * G + PF_ROWS - 1) / PF_ROWS + np : 0;
   const int64_t tiles = pl.pf_tile_cap * hkv;
-  int64_t ks = tiles > 0 ? ((int64_t)max_context_len * tiles / 1024 + PF_KEYS - 1) / PF_KEYS * PF_KEYS : PF_KEYS;
-  ks = ks < 512 ? 512 : ks;
+  int64_t ks = tiles > 0 ? ((int64_t)max_context_len * tiles / CB_PF_TARGET_ITEMS + PF_KEYS - 1) / PF_KEYS * PF_KEYS
+                         : PF_KEYS;
+  ks = ks < CB_PF_MIN_KEYS ? CB_PF_MIN_KEYS : ks;
   pl.pf_split_keys = (int32_t)(ks > PF_MAX_KEYS ? PF_MAX_KEYS : ks);
   const int64_t max_splits = (max_context_len + pl.pf_split_keys - 1) / pl.pf_split_keys;
   pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
