@@ -25,9 +25,10 @@ namespace {
 struct GraphKey {
   int slot;
   int32_t nseq, ndec, ntok, maxctx, stride;
+  int64_t pull;
   const void *q, *k, *v, *out, *ws;
   size_t ws_bytes;
-  auto tie() const { return std::tie(slot, nseq, ndec, ntok, maxctx, stride, q, k, v, out, ws, ws_bytes); }
+  auto tie() const { return std::tie(slot, nseq, ndec, ntok, maxctx, stride, pull, q, k, v, out, ws, ws_bytes); }
   bool operator<(const GraphKey& o) const { return tie() < o.tie(); }
 };
 constexpr size_t kMaxGraphs = 128;
@@ -45,6 +46,11 @@ struct cb_engine {
   int64_t slot_ints = 0;
   // device views of the pending step's metadata
   const int32_t *d_qsl = nullptr, *d_ctx = nullptr, *d_off = nullptr, *d_bt = nullptr, *d_slots = nullptr;
+  // the pinned staging buffer as the device addresses it (null: not mapped,
+  // then the metadata goes up with a copy in the stream)
+  int32_t* meta_host_dev = nullptr;
+  int64_t pull_ints = 0;                 // metadata int32s the append kernel copies up
+  const int32_t* h_slots_dev = nullptr;  // the slot mapping in the staging slot, device address
   bool have_lists = false;  // bf16: the step's work lists were built on the host
   cb::WorkLists lists{};
   // the pending step as launched: the builder's sizes, or their padded shape
@@ -72,12 +78,16 @@ int cb_engine_create(const cb_engine_config* config, cb_engine** out) {
     return cb::fail(CB_ERR_INVALID, "cb_engine_create: bad head counts");
   if (c.head_dim != 64 && c.head_dim != 128) return cb::fail(CB_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (c.dtype != CB_F32 && c.dtype != CB_BF16) return cb::fail(CB_ERR_UNSUPPORTED, "unknown dtype");
-  const int64_t slot_ints = (int64_t)(c.meta_bytes / sizeof(int32_t) / 2);
+  const int64_t slot_ints = (int64_t)(c.meta_bytes / sizeof(int32_t) / 2) & ~int64_t(3);  // 16-byte slots
   if (slot_ints < 16) return cb::fail(CB_ERR_INVALID, "cb_engine_create: metadata buffers too small");
   cb_engine* e = new (std::nothrow) cb_engine();
   if (!e) return cb::fail(CB_ERR_INVALID, "out of host memory");
   e->cfg = c;
   e->slot_ints = slot_ints;
+  if (hipHostGetDevicePointer(reinterpret_cast<void**>(&e->meta_host_dev), c.meta_host, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    e->meta_host_dev = nullptr;
+  }
   int st = cb_builder_create(&c.builder, &e->builder);
   if (st != CB_OK) { delete e; return st; }
   for (int i = 0; i < 2; ++i) {
@@ -107,7 +117,7 @@ cb_builder* cb_engine_builder(cb_engine* e) { return e ? e->builder : nullptr; }
 int cb_engine_set_metadata(cb_engine* e, int32_t* meta_device, int32_t* meta_host, size_t meta_bytes) {
   cb::clear_error();
   if (!e || !meta_device || !meta_host) return cb::fail(CB_ERR_INVALID, "cb_engine_set_metadata: null argument");
-  const int64_t slot_ints = (int64_t)(meta_bytes / sizeof(int32_t) / 2);
+  const int64_t slot_ints = (int64_t)(meta_bytes / sizeof(int32_t) / 2) & ~int64_t(3);
   if (slot_ints < 16) return cb::fail(CB_ERR_INVALID, "cb_engine_set_metadata: buffers too small");
   for (int i = 0; i < 2; ++i)
     if (e->slot_used[i]) (void)hipEventSynchronize(e->copied[i]);
@@ -116,6 +126,10 @@ int cb_engine_set_metadata(cb_engine* e, int32_t* meta_device, int32_t* meta_hos
   e->cfg.meta_host = meta_host;
   e->cfg.meta_bytes = meta_bytes;
   e->slot_ints = slot_ints;
+  if (hipHostGetDevicePointer(reinterpret_cast<void**>(&e->meta_host_dev), meta_host, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    e->meta_host_dev = nullptr;
+  }
   e->slot_used[0] = e->slot_used[1] = false;
   e->slot = 0;
   e->pending = false;
@@ -233,11 +247,19 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
       off = at + lay.bytes / 4;
     }
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(dv, h, off * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess ||
-      hipEventRecord(e->copied[slot], s) != hipSuccess)
-    return cb::fail(CB_ERR_DEVICE, "cb_engine_schedule: metadata upload failed");
-  e->slot_used[slot] = true;
+  if (e->meta_host_dev && e->x_ntok > 0) {
+    // the append kernel that starts the step copies the slot up (and reads
+    // its slot mapping from here); the staging slot stays busy until it ran
+    e->pull_ints = (int64_t)((off + 3) & ~size_t(3));
+    e->h_slots_dev = e->meta_host_dev + (size_t)slot * e->slot_ints + o_sl;
+  } else {
+    e->pull_ints = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(dv, h, off * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipEventRecord(e->copied[slot], s) != hipSuccess)
+      return cb::fail(CB_ERR_DEVICE, "cb_engine_schedule: metadata upload failed");
+    e->slot_used[slot] = true;
+  }
   e->slot = slot;
   e->pending = true;
   e->d_qsl = dv + o_qsl;
@@ -303,9 +325,20 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   if (need > 0 && (!c.workspace || c.workspace_bytes < need))
     return cb::fail(CB_ERR_WORKSPACE, "the scheduled step needs %zu bytes of workspace (have %zu)", need,
                     c.workspace_bytes);
+  const hipStream_t hs0 = static_cast<hipStream_t>(stream);
+  int32_t* dslot = c.meta_device + (size_t)e->slot * e->slot_ints;
   auto launch = [&]() {
-    int rc = cb_kv_append(k_new, v_new, c.k_cache, c.v_cache, e->d_slots, e->x_ntok, c.num_kv_heads,
-                          c.head_dim, c.builder.num_pages, CB_PAGE_SIZE, c.dtype, stream);
+    int rc;
+    if (e->pull_ints > 0) {
+      const hipError_t err = cb::launch_kv_append_pull(
+          k_new, v_new, c.k_cache, c.v_cache, e->h_slots_dev, e->x_ntok, c.num_kv_heads, c.head_dim,
+          c.builder.num_pages, c.dtype == CB_BF16 ? 2 : 4, e->meta_host_dev + (size_t)e->slot * e->slot_ints,
+          dslot, e->pull_ints * 4, hs0);
+      rc = err == hipSuccess ? CB_OK : cb::fail(CB_ERR_DEVICE, "append launch failed: %s", hipGetErrorString(err));
+    } else {
+      rc = cb_kv_append(k_new, v_new, c.k_cache, c.v_cache, e->d_slots, e->x_ntok, c.num_kv_heads, c.head_dim,
+                        c.builder.num_pages, CB_PAGE_SIZE, c.dtype, stream);
+    }
     if (rc != CB_OK) return rc;
     return cb::attention_step_impl(q, c.k_cache, c.v_cache, e->d_bt, e->x_stride, e->d_qsl, e->d_ctx, e->d_off,
                                    e->x_nseq, e->x_ndec, e->x_ntok, e->x_maxctx, c.num_q_heads,
@@ -313,13 +346,22 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
                                    c.builder.sliding_window, c.dtype, out, c.workspace, c.workspace_bytes,
                                    stream, e->have_lists ? &e->lists : nullptr);
   };
+  // with the pull, the staging slot is free once the append kernel has run
+  auto staged = [&]() {
+    if (e->pull_ints == 0) return (int)CB_OK;
+    if (hipEventRecord(e->copied[e->slot], hs0) != hipSuccess)
+      return cb::fail(CB_ERR_DEVICE, "cb_engine_attend: event record failed");
+    e->slot_used[e->slot] = true;
+    return (int)CB_OK;
+  };
   if (!e->capture) {
-    const int st = launch();
+    int st = launch();
+    if (st == CB_OK) st = staged();
     if (st == CB_OK) e->pending = false;
     return st;
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  const GraphKey key{e->slot, e->x_nseq, e->x_ndec, e->x_ntok, e->x_maxctx, e->x_stride,
+  const GraphKey key{e->slot, e->x_nseq, e->x_ndec, e->x_ntok, e->x_maxctx, e->x_stride, e->pull_ints,
                      q, k_new, v_new, out, c.workspace, c.workspace_bytes};
   auto it = e->graphs.find(key);
   if (it == e->graphs.end()) {
@@ -346,8 +388,9 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   if (hipGraphLaunch(it->second, hs) != hipSuccess)
     return cb::fail(CB_ERR_DEVICE, "cb_engine_attend: graph launch failed");
   e->n_replays++;
-  e->pending = false;
-  return CB_OK;
+  const int st = staged();
+  if (st == CB_OK) e->pending = false;
+  return st;
 }
 
 }  // extern "C"

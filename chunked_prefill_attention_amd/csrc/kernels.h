@@ -79,6 +79,12 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
                       int32_t window, const int32_t* qsl, const int32_t* ctx, const int32_t* q_off,
                       void* dst);
 
+// The same append, plus a copy of pull_bytes (a multiple of 16) from pull_src
+// (device-readable host memory) to pull_dst, done by extra blocks of the launch.
+hipError_t launch_kv_append_pull(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* slots, int32_t T, int32_t hkv, int32_t head_dim,
+                                 int32_t num_pages, int32_t elem_bytes, const void* pull_src, void* pull_dst,
+                                 int64_t pull_bytes, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* slots, int32_t num_tokens, int32_t hkv, int32_t head_dim,
                             int32_t num_pages, int32_t elem_bytes, hipStream_t stream);

@@ -14,10 +14,24 @@
 // page.  No arithmetic touches the values (integer loads and stores only).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace cb {
 namespace {
+
+// Optional second job of the same launch: blocks past the append grid copy
+// `pull_n16` 16-byte chunks from `pull_src` (the engine's pinned staging
+// slot, mapped into the device's address space) to `pull_dst` (the device
+// metadata slot).  The step's metadata then reaches the device inside the
+// kernel that starts the step, with no separate copy in the stream.
+struct Pull {
+  const uint4* src;
+  uint4* dst;
+  int64_t n16;
+  int32_t append_blocks;
+};
 
 template <int D, int ES>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ k_new,
@@ -26,7 +40,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
                                                         uint8_t* __restrict__ v_cache,
                                                         const int32_t* __restrict__ slots,
                                                         int32_t num_tokens, int32_t hkv,
-                                                        int32_t num_pages) {
+                                                        int32_t num_pages, Pull pull) {
+  if ((int)blockIdx.x >= pull.append_blocks) {
+    const int64_t nb = (int64_t)gridDim.x - pull.append_blocks;
+    for (int64_t i = ((int64_t)blockIdx.x - pull.append_blocks) * 256 + threadIdx.x; i < pull.n16; i += nb * 256)
+      pull.dst[i] = pull.src[i];
+    return;
+  }
   constexpr int ROWB = D * ES;        // bytes of one token row of one head
   constexpr int CH = ROWB / 16;       // 16-byte chunks per row
   constexpr int LROW = ROWB + 16;     // padded LDS row (spreads the column reads over banks)
@@ -71,13 +91,27 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
 
 template <int D, int ES>
 hipError_t launch(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int32_t* slots,
-                  int32_t T, int32_t hkv, int32_t num_pages, hipStream_t stream) {
+                  int32_t T, int32_t hkv, int32_t num_pages, Pull pull, hipStream_t stream) {
   const int64_t groups = (T + 15) / 16;
-  const dim3 grid((unsigned)(groups * hkv));
+  pull.append_blocks = (int32_t)(groups * hkv);
+  const int64_t pull_blocks = pull.n16 > 0 ? std::min<int64_t>((pull.n16 + 255) / 256, 64) : 0;
+  const dim3 grid((unsigned)(groups * hkv + pull_blocks));
+  if (grid.x == 0) return hipSuccess;
   hipLaunchKernelGGL((kv_append_kernel<D, ES>), grid, dim3(256), 0, stream,
                      static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
-                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), slots, T, hkv, num_pages);
+                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), slots, T, hkv, num_pages,
+                     pull);
   return hipGetLastError();
+}
+
+hipError_t dispatch(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int32_t* slots,
+                    int32_t T, int32_t hkv, int32_t head_dim, int32_t num_pages, int32_t elem_bytes, Pull pull,
+                    hipStream_t stream) {
+  if (head_dim == 128 && elem_bytes == 2) return launch<128, 2>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, pull, stream);
+  if (head_dim == 64 && elem_bytes == 2) return launch<64, 2>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, pull, stream);
+  if (head_dim == 128 && elem_bytes == 4) return launch<128, 4>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, pull, stream);
+  if (head_dim == 64 && elem_bytes == 4) return launch<64, 4>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, pull, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -85,11 +119,17 @@ hipError_t launch(const void* k_new, const void* v_new, void* k_cache, void* v_c
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* slots, int32_t T, int32_t hkv, int32_t head_dim,
                             int32_t num_pages, int32_t elem_bytes, hipStream_t stream) {
-  if (head_dim == 128 && elem_bytes == 2) return launch<128, 2>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, stream);
-  if (head_dim == 64 && elem_bytes == 2) return launch<64, 2>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, stream);
-  if (head_dim == 128 && elem_bytes == 4) return launch<128, 4>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, stream);
-  if (head_dim == 64 && elem_bytes == 4) return launch<64, 4>(k_new, v_new, k_cache, v_cache, slots, T, hkv, num_pages, stream);
-  return hipErrorInvalidValue;
+  return dispatch(k_new, v_new, k_cache, v_cache, slots, T, hkv, head_dim, num_pages, elem_bytes,
+                  Pull{nullptr, nullptr, 0, 0}, stream);
+}
+
+hipError_t launch_kv_append_pull(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* slots, int32_t T, int32_t hkv, int32_t head_dim,
+                                 int32_t num_pages, int32_t elem_bytes, const void* pull_src, void* pull_dst,
+                                 int64_t pull_bytes, hipStream_t stream) {
+  return dispatch(k_new, v_new, k_cache, v_cache, slots, T, hkv, head_dim, num_pages, elem_bytes,
+                  Pull{static_cast<const uint4*>(pull_src), static_cast<uint4*>(pull_dst), pull_bytes / 16, 0},
+                  stream);
 }
 
 }  // namespace cb

@@ -362,14 +362,18 @@ int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out);
  * caller-provided buffers only (it allocates no device or pinned memory):
  *
  *   cb_engine_schedule  host: builder step, descriptor written into a pinned
- *                       staging slot, one async host-to-device copy on
- *                       `stream` into a device metadata slot;
- *   cb_engine_attend    device: cb_kv_append of the step's rows, then
+ *                       staging slot;
+ *   cb_engine_attend    device: one launch appends the step's K/V rows and,
+ *                       in extra workgroups, copies the staging slot into a
+ *                       device metadata slot (the kernel reads the pinned
+ *                       buffer through its device mapping); then
  *                       cb_attention_step, on `stream`.
  *
- * Two staging/metadata slots alternate, so the host can schedule step N+1
- * while step N runs; before reusing a slot the engine waits (on the host) for
- * the copy that last read it.  All steps of one engine must be enqueued on
+ * When the pinned buffer has no device mapping, cb_engine_schedule instead
+ * enqueues a host-to-device copy of the slot on `stream`.  Two
+ * staging/metadata slots alternate, so the host can schedule step N+1 while
+ * step N runs; before reusing a staging slot the engine waits (on the host)
+ * for the kernel or copy that last read it.  All steps of one engine must be enqueued on
  * one stream.  The caller computes q, k_new, v_new of the scheduled tokens
  * (rows in the descriptor's order) between the two calls.
  * ------------------------------------------------------------------------- */
