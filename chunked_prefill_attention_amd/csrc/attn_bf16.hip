@@ -46,6 +46,7 @@
 // select and their V entries zeroed, so garbage or NaN there never reaches
 // the output.
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <vector>
 
 #include <algorithm>
@@ -90,9 +91,13 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_PF_THREADS
 #define CB_PF_THREADS 256
 #endif
+#ifndef CB_PF_NB           // 32-row blocks per prefill wave (2: one wave per SIMD)
+#define CB_PF_NB 1
+#endif
 constexpr int PF_THREADS = CB_PF_THREADS;   // threads of a prefill workgroup
 constexpr int PF_WAVES = PF_THREADS / 64;
-constexpr int PF_ROWS = PF_WAVES * 32;      // query rows per prefill workgroup (32 per wave)
+constexpr int PF_NB = CB_PF_NB;
+constexpr int PF_ROWS = PF_WAVES * 32 * PF_NB;  // query rows per prefill workgroup
 constexpr int PF_KEYS = 64;   // keys per prefill tile (4 pages)
 constexpr int PF_MAX_PAGES = 512;                          // page ids one prefill item stages in LDS
 constexpr int PF_MAX_KEYS = (PF_MAX_PAGES - 4) * 16 / PF_KEYS * PF_KEYS;  // largest key range per item
@@ -107,6 +112,7 @@ struct Params {
   const int32_t* ctx_lens;
   const int32_t* q_off;
   uint16_t* out;
+  int4* hdr;             // (live prefill items, live decode items, block order, 0)
   int4* dec_items;       // (sequence, split, context length, query row); sequence -1 = no work
   int4* pf_items;        // (sequence, row tile, key split, partial slot); -1 = no work
   int4* pf_tiles;        // (sequence, row tile, first item, number of splits); -1 = none
@@ -123,6 +129,7 @@ struct Params {
   int32_t split_pages;   // pages per decode item
   int32_t pf_split_keys; // keys per prefill item (multiple of PF_KEYS)
   int32_t pf_blocks;     // grid blocks reserved for prefill items
+  int32_t slots;         // workgroups of the mixed launch the device holds at once
   int32_t dec_cap, pf_tile_cap, pf_item_cap;
   int32_t comb_dec_blocks;
   int32_t window;        // sliding window in tokens; 0 = none
@@ -148,6 +155,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, b16x2));
+}
+
+// acc + the sum of eight bf16 values (four packed pairs), one dot2 with (1, 1) per pair
+__device__ __forceinline__ float sum_bf16x8(uint4 v, float acc) {
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  const b16x2 one = __builtin_bit_cast(b16x2, 0x3F803F80u);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, v.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, v.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, v.z), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b16x2, v.w), one, acc, false);
 }
 
 // Reductions over lane pairs (l, l^32) and (l, l^16) through the cross-lane
@@ -284,6 +301,16 @@ __host__ __device__ __forceinline__ int tile_splits(int tile, int L, int G, int 
   return (tile_key_end(tile, L, G, ctx, off) - tile_key_base(tile, G, off, window) + split_keys - 1) / split_keys;
 }
 
+// Block order of the mixed launch.  When the live prefill workgroups fit in
+// one round of the device's workgroup slots they go first (they all start at
+// once and finish early, decodes fill the rest); when they need several
+// rounds, going first would run the MFMA-bound and the HBM-bound work one
+// after the other, so prefill and decode blocks are interleaved instead and
+// most CUs hold one of each.
+__host__ __device__ inline int mix_order(int64_t pf_live_items, int64_t dec_live_items, int hkv, int slots) {
+  return (pf_live_items * hkv > slots && dec_live_items > 0) ? 1 : 0;
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   __shared__ int sh[40];
   const int tid = threadIdx.x;
@@ -381,6 +408,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   }
   for (int i = tcarry + tid; i < p.pf_tile_cap; i += 1024) p.pf_tiles[i] = make_int4(-1, 0, 0, 0);
   for (int i = icarry + tid; i < p.pf_item_cap; i += 1024) p.pf_items[i] = make_int4(-1, 0, 0, 0);
+  if (tid == 0) {
+    const int pl = min(icarry, p.pf_item_cap), dl = min(dec_total, p.dec_cap);
+    *p.hdr = make_int4(pl, dl, mix_order(pl, dl, p.hkv, p.slots), 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -571,24 +602,28 @@ __device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const 
                                          int ctx, int kvh, int tid) {
   // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens.
   // Chunk i of a thread lies in page (tid + PF_THREADS i) / 2D of the tile,
-  // the same page for the whole wavefront; its id comes from LDS (-1 = no page).
+  // the same page for the whole wavefront; the tile's 4 page ids come from LDS
+  // in one read (-1 = no page).
+  const int4 ids = *reinterpret_cast<const int4*>(pids + (kt - kt0) * 4);
 #pragma unroll
   for (int i = 0; i < PfStage<D>::N; ++i) {
     const int e = tid + PF_THREADS * i;
     const int pgl = e / (2 * D), rem = e % (2 * D);
-    const int pg = kt * 4 + pgl;
     // pages past the context (id -1) read page 0; their keys are masked by
     // the causal test and their V tokens zeroed below (n <= 0)
-    const int ph = __builtin_amdgcn_readfirstlane(pids[(kt - kt0) * 4 + pgl]);
+    const int id = pgl == 0 ? ids.x : pgl == 1 ? ids.y : pgl == 2 ? ids.z : ids.w;
+    const int ph = __builtin_amdgcn_readfirstlane(id);
     const int phys = (unsigned)ph < (unsigned)p.num_pages ? ph : 0;
     const size_t slab = (size_t)phys * p.hkv + kvh;
-    const uint16_t* kb = uniform_ptr(p.k_cache + slab * 16 * D);
-    const uint16_t* vb = uniform_ptr(p.v_cache + slab * D * 16);
-    const int r = rem / (D / 8), c16 = rem % (D / 8);
-    const uint4 kv = stream_load(reinterpret_cast<const uint4*>(kb + r * D + c16 * 8));
-    const int dr = rem >> 1, hf = rem & 1;
-    st.k[i] = kv;
-    st.v[i] = stream_load(reinterpret_cast<const uint4*>(vb + dr * 16 + hf * 8));
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.k_cache + slab * 16 * D));
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.v_cache + slab * D * 16));
+    // the chunk's byte offset in both slabs: K row rem / (D/8), 8-dim chunk rem % (D/8);
+    // V row rem / 2, 8-token half rem % 2.  Both are 16 rem bytes.  An unsigned
+    // 32-bit offset from a uniform base lets the load take its scalar-base form.
+    uint32_t off = 16u * (uint32_t)rem;
+    asm volatile("" : "+v"(off));  // keeps the offset 32-bit at the load (not hoisted as a 64-bit value)
+    st.k[i] = stream_load(reinterpret_cast<const uint4*>(kb + off));
+    st.v[i] = stream_load(reinterpret_cast<const uint4*>(vb + off));
   }
 }
 
@@ -601,6 +636,9 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
   using Lds = PfLds<D>;
   uint8_t* kl = stage;
   uint8_t* vl = stage + Lds::K_BYTES;
+  // uniform: only the tile that holds the context end (or the window floor) masks
+  const bool tail = (kt + 1) * PF_KEYS > ctx;
+  const bool below = WIN && kt * PF_KEYS < kfloor;
 #pragma unroll
   for (int i = 0; i < PfStage<D>::N; ++i) {
     const int e = tid + PF_THREADS * i;
@@ -612,14 +650,14 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
     uint4 vv = st.v[i];
     const int k8 = (kt * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
     const int n = ctx - k8;                          // valid tokens among these 8
-    if (n < 8) {
+    if (tail && n < 8) {
       vv.x = keep16(vv.x, 0, n);
       vv.y = keep16(vv.y, 2, n);
       vv.z = keep16(vv.z, 4, n);
       vv.w = keep16(vv.w, 6, n);
     }
     const int nlo = kfloor - k8;                     // tokens below the first key
-    if (WIN && nlo > 0) {
+    if (below && nlo > 0) {
       vv.x = drop16(vv.x, 0, nlo);
       vv.y = drop16(vv.y, 2, nlo);
       vv.z = drop16(vv.z, 4, nlo);
@@ -632,6 +670,7 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
 template <int D, bool WIN>
 __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* smem) {
   using Lds = PfLds<D>;
+  constexpr int NB = PF_NB;   // 32-row blocks per wave: every K/V fragment read from LDS feeds NB MFMAs
   const int kvh = b % p.hkv;
   const int j = b / p.hkv;
   if (j >= p.pf_item_cap) return;
@@ -653,22 +692,29 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, gg = lane >> 5;
   const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // l32 with bits 2, 3 swapped
-
-  const int row = tile * PF_ROWS + wv * 32 + l32;
-  const bool rvalid = row < R;
-  const int qi = row / G;
-  const int hh = row - qi * G;
-  const int kcap = min(off + qi, ctx - 1);              // last key this row may see
   const int W = WIN ? p.window : 0;
-  const int kfirst = window_first_key(off + qi, W);     // first key this row may see
+
+  // this lane's rows: block nb of the wave holds rows wave_base + 32 nb + l32
+  const int wave_base = tile * PF_ROWS + wv * 32 * NB;
+  int qi[NB], hh[NB], kcap[NB], kfirst[NB];
+  bool rvalid[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = wave_base + 32 * nb + l32;
+    rvalid[nb] = row < R;
+    qi[nb] = row / G;
+    hh[nb] = row - qi[nb] * G;
+    kcap[nb] = min(off + qi[nb], ctx - 1);             // last key this row may see
+    kfirst[nb] = window_first_key(off + qi[nb], W);    // first key this row may see
+  }
 
   // this item's key range, in whole 64-key tiles, from the tile's first row's window
   const int k_lo = (WIN ? tile_key_base(tile, G, off, W) : 0) + ks * p.pf_split_keys;
   const int k_hi = min(k_lo + p.pf_split_keys, tile_key_end(tile, L, G, ctx, off));
   const int kt0 = k_lo / PF_KEYS, kt1 = (k_hi + PF_KEYS - 1) / PF_KEYS;
   const int kfloor = window_first_key(off + tile * PF_ROWS / G, W);  // no row of the tile sees below
-  const int w_first_row = tile * PF_ROWS + wv * 32;
-  const int w_last_row = min(w_first_row + 31, R - 1);
+  const int w_first_row = wave_base;
+  const int w_last_row = min(wave_base + 32 * NB - 1, R - 1);
   const int w_kend = (w_first_row < R) ? min(ctx, off + w_last_row / G + 1) : 0;
   const int w_kfull = min(ctx, off + w_first_row / G + 1);  // keys below are visible to every row...
   const int w_klo_min = window_first_key(off + w_first_row / G, W);  // ...and at or above the window
@@ -688,15 +734,16 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   // in the second LDS stage and tile kt is computed.  Fetches past the last
   // tile re-read it (clamped), so every iteration issues the same loads and
   // the compiler never has to drain the one still in flight.
-  // the query fragment first: it is waited for once, here, while the first
-  // two K/V tiles stay in flight (a load still pending at the loop header
-  // would make the compiler wait inside the loop, draining the pipeline)
-  bf16x8 qf[NK];
-  {
-    const uint16_t* qrow = p.q + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + 8 * gg;
+  // The query fragments first: they are waited for once, here, while the
+  // first two K/V tiles stay in flight (a load still pending at the loop
+  // header would make the compiler wait inside the loop, draining the pipeline).
+  bf16x8 qf[NB][NK];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const uint16_t* qrow = p.q + ((size_t)(t0 + qi[nb]) * p.hq + kvh * G + hh[nb]) * D + 8 * gg;
 #pragma unroll
     for (int cc = 0; cc < NK; ++cc)
-      qf[cc] = as_bf16x8(rvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
+      qf[nb][cc] = as_bf16x8(rvalid[nb] ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
   }
   PfStage<D> sa, sb;
   const int klast = kt1 - 1;
@@ -705,16 +752,23 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), kt0, ctx, kvh, tid);
   }
 #pragma unroll
-  for (int cc = 0; cc < NK; ++cc) {
-    const uint4 qq = __builtin_bit_cast(uint4, qf[cc]);
-    asm volatile("" ::"v"(qq.x), "v"(qq.y), "v"(qq.z), "v"(qq.w));
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int cc = 0; cc < NK; ++cc) {
+      const uint4 qq = __builtin_bit_cast(uint4, qf[nb][cc]);
+      asm volatile("" ::"v"(qq.x), "v"(qq.y), "v"(qq.z), "v"(qq.w));
+    }
+  floatx16 o[NB][NO];
+  float m[NB], l[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int dt = 0; dt < NO; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nb][dt][r] = 0.f;
+    m[nb] = -INFINITY;
+    l[nb] = 0.f;
   }
-  floatx16 o[NO];
-#pragma unroll
-  for (int dt = 0; dt < NO; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
   const float c = p.scale_log2;
 
   uint8_t* stage0 = smem;
@@ -730,72 +784,89 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       // (bits 2 and 3 of m swapped), so that lane (l32, gg) receives, for
       // r = 0..15, key 16(r/8) + 8gg + r%8 of its subtile: the 8 consecutive
       // keys the P V product takes from it, with no exchange between lanes.
-      floatx16 sc[2];
+      floatx16 sc[NB][2];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[sub][r] = 0.f;
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[nb][sub][r] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < NK; ++cc) {
           const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + krow) * Lds::KROW + (16 * cc + 8 * gg) * 2);
-          sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[cc], sc[sub], 0, 0, 0);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            sc[nb][sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[nb][cc], sc[nb][sub], 0, 0, 0);
         }
       }
       // straddles this wave's diagonal (or the context end), or its window's lower edge
       if (kbase + PF_KEYS > w_kfull || (WIN && kbase < w_klo_max)) {
 #pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kbase + sub * 32 + 16 * (r >> 3) + 8 * gg + (r & 7);
+              sc[nb][sub][r] = (key <= kcap[nb] && (!WIN || key >= kfirst[nb])) ? sc[nb][sub][r] : -INFINITY;
+            }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = -INFINITY;
+#pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + sub * 32 + 16 * (r >> 3) + 8 * gg + (r & 7);
-            sc[sub][r] = (key <= kcap && (!WIN || key >= kfirst)) ? sc[sub][r] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nb][sub][r]);
+        mx = pair_max32(mx);
+        const bool raise = (mx - m[nb]) * c > CB_RESCALE_SLACK;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+          const float alpha = raise ? fast_exp2((m[nb] - mx) * c) : 1.f;
+          l[nb] *= alpha;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
-      mx = pair_max32(mx);
-      const bool raise = (mx - m) * c > CB_RESCALE_SLACK;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? fast_exp2((m - mx) * c) : 1.f;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NO; ++dt) o[dt] *= alpha;
-        m = raise ? mx : m;
-      }
-      const float nm = neg_scaled(m, c);
-      float rs = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(sc[sub][r], c, nm));
-          sc[sub][r] = pv;
-          rs += pv;
+          for (int dt = 0; dt < NO; ++dt) o[nb][dt] *= alpha;
+          m[nb] = raise ? mx : m[nb];
         }
-      l += rs;
+        const float nm = neg_scaled(m[nb], c);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[nb][sub][r] = fast_exp2(fmaf(sc[nb][sub][r], c, nm));
+      }
 
       // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile):
       // lane (l32, gg) holds P for keys 8gg..8gg+7 of the page, and reads V
-      // for the same keys as one contiguous 16-byte load.
+      // for the same keys as one contiguous 16-byte load.  The row sum is
+      // taken from the same bf16 P (a two-term dot product with ones per
+      // packed pair), so the normaliser weighs exactly what P V does.
+      float rsum[NB][2];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) rsum[nb][0] = rsum[nb][1] = 0.f;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int r0 = 8 * half;
-          const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
-                                      pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
-                                      pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
-                                      pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
+          uint4 pb[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            pb[nb] = make_uint4(pack_bf16x2(sc[nb][sub][r0 + 0], sc[nb][sub][r0 + 1]),
+                                pack_bf16x2(sc[nb][sub][r0 + 2], sc[nb][sub][r0 + 3]),
+                                pack_bf16x2(sc[nb][sub][r0 + 4], sc[nb][sub][r0 + 5]),
+                                pack_bf16x2(sc[nb][sub][r0 + 6], sc[nb][sub][r0 + 7]));
+            rsum[nb][half] = sum_bf16x8(pb[nb], rsum[nb][half]);
+          }
           const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
 #pragma unroll
           for (int dt = 0; dt < NO; ++dt) {
             const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + 16 * gg);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              o[nb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[nb]), o[nb][dt], 0, 0, 0);
           }
         }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) l[nb] += rsum[nb][0] + rsum[nb][1];
     }
   };
   for (int kt = kt0; kt < kt1; kt += 2) {
@@ -810,29 +881,32 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     __syncthreads();
   }
 
-  l = pair_sum32(l);
-  if (!rvalid) return;
-  if (nsplit == 1) {
-    const float inv = 1.f / l;
-    uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D;
 #pragma unroll
-    for (int dt = 0; dt < NO; ++dt)
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = pair_sum32(l[nb]);
+    if (!rvalid[nb]) continue;
+    if (nsplit == 1) {
+      const float inv = 1.f / lt;
+      uint16_t* orow = p.out + ((size_t)(t0 + qi[nb]) * p.hq + kvh * G + hh[nb]) * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint2 v = make_uint2(pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv),
-                                   pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv));
-        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
-      }
-  } else {
-    const size_t prow = ((size_t)slot * p.hkv + kvh) * PF_ROWS + wv * 32 + l32;
-    float* po = p.pf_o + prow * D;
+      for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < NO; ++dt)
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const uint2 v = make_uint2(pack_bf16x2(o[nb][dt][4 * q4 + 0] * inv, o[nb][dt][4 * q4 + 1] * inv),
+                                     pack_bf16x2(o[nb][dt][4 * q4 + 2] * inv, o[nb][dt][4 * q4 + 3] * inv));
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
+        }
+    } else {
+      const size_t prow = ((size_t)slot * p.hkv + kvh) * PF_ROWS + wv * 32 * NB + 32 * nb + l32;
+      float* po = p.pf_o + prow * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<floatx4*>(po + 32 * dt + 8 * q4 + 4 * gg) =
-            floatx4{o[dt][4 * q4 + 0], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
-    if (gg == 0) p.pf_ml[prow] = make_float2(m, l);
+      for (int dt = 0; dt < NO; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<floatx4*>(po + 32 * dt + 8 * q4 + 4 * gg) =
+              floatx4{o[nb][dt][4 * q4 + 0], o[nb][dt][4 * q4 + 1], o[nb][dt][4 * q4 + 2], o[nb][dt][4 * q4 + 3]};
+      if (gg == 0) p.pf_ml[prow] = make_float2(m[nb], lt);
+    }
   }
 }
 
@@ -842,13 +916,39 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 // LDS nor the prefill registers and runs at higher occupancy.
 // ---------------------------------------------------------------------------
 template <int D, bool WIN>
-__global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kernel(Params p) {
+__global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS / PF_NB) void attn_mixed_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
-  if ((int)blockIdx.x < p.pf_blocks) {
-    prefill_tile<D, WIN>(p, blockIdx.x, smem);
+  const int b = blockIdx.x;
+  const int np = p.pf_blocks, nd = (int)gridDim.x - np;
+  // live blocks first, in the order the header names; the blocks the caps
+  // reserve beyond the live work (they find no item and return) come last
+  const int4 h = *p.hdr;
+  const int lp = min(h.x * p.hkv, np);
+  const int ld = min((h.y * p.hkv + PF_WAVES - 1) / PF_WAVES, nd);
+  int pf = -1, dec = -1;
+  if (b < lp + ld) {
+    // interleaved: groups of 8 alternate; blocks go to the XCDs round-robin,
+    // so every prefill index stays on the XCD it has in prefill-first order
+    const int m8 = h.z ? (min(lp, ld) & ~7) : 0;
+    if (b < 2 * m8) {
+      const int grp = b >> 4, w = b & 15;
+      if (w < 8) pf = 8 * grp + w;
+      else dec = 8 * grp + w - 8;
+    } else {
+      const int r = b - 2 * m8;
+      if (r < lp - m8) pf = m8 + r;
+      else dec = m8 + r - (lp - m8);
+    }
+  } else {
+    const int r = b - lp - ld;
+    if (r < np - lp) pf = lp + r;
+    else dec = ld + r - (np - lp);
+  }
+  if (pf >= 0) {
+    prefill_tile<D, WIN>(p, pf, smem);
     return;
   }
-  decode_wave<D, WIN>(p, ((int)blockIdx.x - p.pf_blocks) * PF_WAVES + (threadIdx.x >> 6));
+  decode_wave<D, WIN>(p, dec * PF_WAVES + (threadIdx.x >> 6));
 }
 
 template <int D, bool WIN>
@@ -987,6 +1087,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.ctx_lens = a.ctx_lens;
   p.q_off = a.q_offsets;
   p.out = static_cast<uint16_t*>(a.out);
+  p.hdr = reinterpret_cast<int4*>(ws + pl.off_hdr);
   p.dec_items = reinterpret_cast<int4*>(ws + pl.off_dec_items);
   p.pf_items = reinterpret_cast<int4*>(ws + pl.off_pf_items);
   p.pf_tiles = reinterpret_cast<int4*>(ws + pl.off_pf_tiles);
@@ -1013,12 +1114,14 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
   const int64_t dec_blocks = (pl.dec_cap * a.hkv + PF_WAVES - 1) / PF_WAVES;
   p.pf_blocks = (int32_t)pf_blocks;
+  p.slots = pl.slots;
   const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
   const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
   const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv * (PF_ROWS / CP_ROWS) : 0;
   p.comb_dec_blocks = (int32_t)comb_dec;
 
   if (lists) {  // built by the caller: read them where they were uploaded
+    p.hdr = const_cast<int4*>(static_cast<const int4*>(lists->hdr));
     p.dec_items = const_cast<int4*>(static_cast<const int4*>(lists->dec_items));
     p.pf_items = const_cast<int4*>(static_cast<const int4*>(lists->pf_items));
     p.pf_tiles = const_cast<int4*>(static_cast<const int4*>(lists->pf_tiles));
@@ -1046,6 +1149,18 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 256 if unknown).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq, int32_t hkv,
                    int32_t head_dim, int32_t max_context_len) {
   Bf16Plan pl{};
@@ -1072,8 +1187,11 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t max_splits = (max_context_len + pl.pf_split_keys - 1) / pl.pf_split_keys;
   pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
   pl.pf_may_split = max_splits > 1;
+  pl.hkv = hkv;
+  pl.slots = 2 * device_cus();  // two prefill-sized workgroups per CU (LDS bound)
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 0;
+  pl.off_hdr = off;         off = align(off + 16);
   pl.off_dec_items = off;   off = align(off + (size_t)pl.dec_cap * 16);
   pl.off_pf_items = off;    off = align(off + (size_t)pl.pf_item_cap * 16);
   pl.off_pf_tiles = off;    off = align(off + (size_t)pl.pf_tile_cap * 16);
@@ -1100,6 +1218,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
   auto align = [](size_t x) { return (x + 15) & ~size_t(15); };
   WorkListLayout L{};
   size_t off = 0;
+  L.hdr = off;        off = align(off + 16);
   L.dec_items = off;  off = align(off + (size_t)pl.dec_cap * 16);
   L.pf_items = off;   off = align(off + (size_t)pl.pf_item_cap * 16);
   L.pf_tiles = off;   off = align(off + (size_t)pl.pf_tile_cap * 16);
@@ -1175,6 +1294,9 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
   }
   for (int64_t i = nt; i < pl.pf_tile_cap; ++i) pft[i] = make_int4(-1, 0, 0, 0);
   for (int64_t i = ni; i < pl.pf_item_cap; ++i) pfi[i] = make_int4(-1, 0, 0, 0);
+  const int64_t pl_live = std::min<int64_t>(ni, pl.pf_item_cap), dl_live = std::min<int64_t>(n, pl.dec_cap);
+  *reinterpret_cast<int4*>(base + L.hdr) =
+      make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), 0);
 }
 
 }  // namespace cb

@@ -238,6 +238,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
       cb::build_work_lists(pl, e->x_nseq, e->x_ndec, e->cfg.num_q_heads / e->cfg.num_kv_heads,
                            e->cfg.builder.sliding_window, h + o_qsl, h + o_ctx, h + o_off, h + at);
       const uint8_t* db = reinterpret_cast<const uint8_t*>(dv + at);
+      e->lists.hdr = db + lay.hdr;
       e->lists.dec_items = db + lay.dec_items;
       e->lists.pf_items = db + lay.pf_items;
       e->lists.pf_tiles = db + lay.pf_tiles;

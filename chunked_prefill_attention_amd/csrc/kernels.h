@@ -48,7 +48,9 @@ struct Bf16Plan {
   int64_t dec_cap;        // bound on (sequence, split) decode items
   int64_t pf_tile_cap;    // bound on (sequence, 128-row tile) prefill tiles
   int64_t pf_item_cap;    // bound on (tile, key split) prefill items
-  size_t off_dec_items, off_pf_items, off_pf_tiles, off_dec_first, off_dec_rem;
+  int32_t hkv;            // KV heads (workgroups per prefill item)
+  int32_t slots;          // workgroups of the mixed launch the device holds at once
+  size_t off_hdr, off_dec_items, off_pf_items, off_pf_tiles, off_dec_first, off_dec_rem;
   size_t off_dec_ml, off_dec_o, off_pf_ml, off_pf_o;
   size_t bytes;
 };
@@ -59,6 +61,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
 // the host and uploads them with the step's metadata); when given, the
 // device plan kernel is skipped.
 struct WorkLists {
+  const void* hdr;           // int4: (live prefill items, live decode items, block order, 0)
   const void* dec_items;     // int4 [dec_cap]: (sequence, split, context, query row); -1 = none
   const void* pf_items;      // int4 [pf_item_cap]: (sequence, row tile, key split, partial slot)
   const void* pf_tiles;      // int4 [pf_tile_cap]: (sequence, row tile, first item, splits)
@@ -68,7 +71,7 @@ struct WorkLists {
 
 // Host layout of the work lists: byte offsets inside one buffer (16-byte aligned).
 struct WorkListLayout {
-  size_t dec_items, pf_items, pf_tiles, dec_first, dec_rem, bytes;
+  size_t hdr, dec_items, pf_items, pf_tiles, dec_first, dec_rem, bytes;
 };
 WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes);
 
