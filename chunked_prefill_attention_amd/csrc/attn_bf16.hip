@@ -70,8 +70,14 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_DEC_WAVES_PER_SIMD
 #define CB_DEC_WAVES_PER_SIMD 2
 #endif
-#ifndef CB_NONTEMPORAL_KV
-#define CB_NONTEMPORAL_KV 0
+#ifndef CB_DEC_MIN_WAVES     // decode splits: the longest that still gives this many wavefronts
+#define CB_DEC_MIN_WAVES 8192
+#endif
+#ifndef CB_NT_DECODE        // decode-only launch: K/V page loads with the non-temporal hint
+#define CB_NT_DECODE 1
+#endif
+#ifndef CB_NT_PREFILL       // prefill K/V tile loads with the non-temporal hint (tiles are re-read)
+#define CB_NT_PREFILL 0
 #endif
 // threads per workgroup of the decode-only kernel (64 or 256)
 #ifndef CB_DEC_WG
@@ -209,28 +215,26 @@ __device__ __forceinline__ float neg_scaled(float m, float c) { return m == -INF
 
 // Loads through the global address space (pointers rebuilt from SGPR halves
 // would otherwise become generic "flat" accesses, which the compiler must
-// order against LDS traffic too).  K/V page loads are streaming: each byte is
-// used once per launch.
+// order against LDS traffic too).  NT selects the non-temporal hint: decode
+// pages are read once per launch, prefill key tiles once per row tile.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const u32x4 gu32x4;
 typedef __attribute__((address_space(1))) const u32x2 gu32x2;
-__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+template <bool NT>
+__device__ __forceinline__ uint4 kv_load(const uint4* p) {
   gu32x4* g = (gu32x4*)p;
-#if CB_NONTEMPORAL_KV
-  const u32x4 v = __builtin_nontemporal_load(g);
-#else
-  const u32x4 v = *g;
-#endif
+  u32x4 v;
+  if constexpr (NT) v = __builtin_nontemporal_load(g);
+  else v = *g;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ uint2 stream_load(const uint2* p) {
+template <bool NT>
+__device__ __forceinline__ uint2 kv_load(const uint2* p) {
   gu32x2* g = (gu32x2*)p;
-#if CB_NONTEMPORAL_KV
-  const u32x2 v = __builtin_nontemporal_load(g);
-#else
-  const u32x2 v = *g;
-#endif
+  u32x2 v;
+  if constexpr (NT) v = __builtin_nontemporal_load(g);
+  else v = *g;
   return make_uint2(v.x, v.y);
 }
 
@@ -439,7 +443,7 @@ __device__ __forceinline__ const T* uniform_ptr(const T* ptr) {
 // join).  `phys` is wave-uniform; an id out of range (a broken precondition,
 // or the slots past the end of the split, which are never computed) reads
 // page 0 instead.
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void decode_issue(DecodeBuf<D>& B, const Params& p, int phys, int kvh,
                                              int koff, int voff) {
   const int pg = (unsigned)phys < (unsigned)p.num_pages ? phys : 0;
@@ -447,9 +451,9 @@ __device__ __forceinline__ void decode_issue(DecodeBuf<D>& B, const Params& p, i
   const uint16_t* kb = uniform_ptr(p.k_cache + slab * 16 * D);
   const uint16_t* vb = uniform_ptr(p.v_cache + slab * D * 16);
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) B.k[c] = stream_load(reinterpret_cast<const uint4*>(kb + koff + 32 * c));
+  for (int c = 0; c < D / 32; ++c) B.k[c] = kv_load<NT>(reinterpret_cast<const uint4*>(kb + koff + 32 * c));
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) B.v[t] = stream_load(reinterpret_cast<const uint2*>(vb + voff + 256 * t));
+  for (int t = 0; t < D / 16; ++t) B.v[t] = kv_load<NT>(reinterpret_cast<const uint2*>(vb + voff + 256 * t));
 }
 
 // WIN: a sliding window is set (the full-attention instance carries none of its code)
@@ -503,7 +507,9 @@ __device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx,
     o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(B.v[t]), as_short4(pk), o[t], 0, 0, 0);
 }
 
-template <int D, bool WIN>
+// NT: page loads with the non-temporal hint (the decode-only launch; in the
+// mixed launch plain loads measured slightly faster)
+template <int D, bool WIN, bool NT>
 __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int kvh = w % p.hkv;
   const int j = w / p.hkv;
@@ -537,10 +543,10 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   constexpr int PF = CB_DEC_PREFETCH;
   constexpr int NB = PF + 1;
   DecodeBuf<D> buf[NB];
-  decode_issue<D>(buf[0], p, pg0 < pg1 ? first_page : -1, kvh, koff, voff);
+  decode_issue<D, NT>(buf[0], p, pg0 < pg1 ? first_page : -1, kvh, koff, voff);
 #pragma unroll
   for (int r = 1; r < PF; ++r)
-    decode_issue<D>(buf[r], p, pg0 + r < pg1 ? __builtin_amdgcn_readlane(my_page, r) : -1, kvh, koff, voff);
+    decode_issue<D, NT>(buf[r], p, pg0 + r < pg1 ? __builtin_amdgcn_readlane(my_page, r) : -1, kvh, koff, voff);
 
   bf16x8 qf[D / 32];
   {
@@ -562,7 +568,7 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
       const int nxt = cur + PF;
       // readlane's lane index wraps past 63; the page is then unused (nxt >= pg1)
       const int phys = nxt < pg1 ? __builtin_amdgcn_readlane(my_page, (nxt - pg0) & 63) : -1;
-      decode_issue<D>(buf[(r + PF) % NB], p, phys, kvh, koff, voff);
+      decode_issue<D, NT>(buf[(r + PF) % NB], p, phys, kvh, koff, voff);
       if (cur < pg1) decode_compute<D, WIN>(buf[r], cur, ctx, lo, g, qf, o, m, l, c);
     }
   }
@@ -622,8 +628,8 @@ __device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const 
     // 32-bit offset from a uniform base lets the load take its scalar-base form.
     uint32_t off = 16u * (uint32_t)rem;
     asm volatile("" : "+v"(off));  // keeps the offset 32-bit at the load (not hoisted as a 64-bit value)
-    st.k[i] = stream_load(reinterpret_cast<const uint4*>(kb + off));
-    st.v[i] = stream_load(reinterpret_cast<const uint4*>(vb + off));
+    st.k[i] = kv_load<CB_NT_PREFILL>(reinterpret_cast<const uint4*>(kb + off));
+    st.v[i] = kv_load<CB_NT_PREFILL>(reinterpret_cast<const uint4*>(vb + off));
   }
 }
 
@@ -948,12 +954,12 @@ __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS / PF_NB) void attn_mix
     prefill_tile<D, WIN>(p, pf, smem);
     return;
   }
-  decode_wave<D, WIN>(p, dec * PF_WAVES + (threadIdx.x >> 6));
+  decode_wave<D, WIN, false>(p, dec * PF_WAVES + (threadIdx.x >> 6));
 }
 
 template <int D, bool WIN>
 __global__ __launch_bounds__(CB_DEC_WG, CB_DEC_WAVES_PER_SIMD) void attn_decode_kernel(Params p) {
-  decode_wave<D, WIN>(p, (int)blockIdx.x * (CB_DEC_WG / 64) + (threadIdx.x >> 6));
+  decode_wave<D, WIN, CB_NT_DECODE>(p, (int)blockIdx.x * (CB_DEC_WG / 64) + (threadIdx.x >> 6));
 }
 
 // ---------------------------------------------------------------------------
@@ -1172,7 +1178,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t lanes = (int64_t)num_decodes * hkv;
   pl.split_pages = 8;
   for (int sp : {64, 32, 16}) {
-    if (lanes * ((max_pages + sp - 1) / sp) >= 8192) { pl.split_pages = sp; break; }
+    if (lanes * ((max_pages + sp - 1) / sp) >= CB_DEC_MIN_WAVES) { pl.split_pages = sp; break; }
   }
   pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);
   // prefill: row tiles bound by the query tokens; key ranges cut so that about
