@@ -145,7 +145,7 @@ struct Params {
 template <int D>
 struct PfLds {
   static constexpr int KROW = D * 2 + 16;  // padded K row (bytes) in LDS
-  static constexpr int VROW = 32;          // (page, dim) row of 16 tokens (bytes): 16-byte reads, no conflicts
+  static constexpr int VROW = 32;          // (page, dim) row of 16 tokens (bytes), halves swapped on rows with bit 3 set
   static constexpr int K_BYTES = PF_KEYS * KROW;
   static constexpr int V_BYTES = (PF_KEYS / 16) * D * VROW;
   static constexpr int STAGE = K_BYTES + V_BYTES;
@@ -652,7 +652,9 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
     const int r = rem / (D / 8), c16 = rem % (D / 8);
     *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = st.k[i];
     const int dr = rem >> 1, hf = rem & 1;
-    uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + hf * 16;  // tokens 8hf..8hf+7, natural order
+    // tokens 8hf..8hf+7 of row dr, the halves of rows with bit 3 set swapped
+    // (rows r and r + 8 are 256 bytes apart: same banks for the same half)
+    uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + 16 * (hf ^ ((dr >> 3) & 1));
     uint4 vv = st.v[i];
     const int k8 = (kt * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
     const int n = ctx - k8;                          // valid tokens among these 8
@@ -698,6 +700,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, gg = lane >> 5;
   const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);  // l32 with bits 2, 3 swapped
+  const int vhalf = 16 * (gg ^ ((l32 >> 3) & 1));  // this lane's 16-byte half of a V row in LDS
   const int W = WIN ? p.window : 0;
 
   // this lane's rows: block nb of the wave holds rows wave_base + 32 nb + l32
@@ -865,7 +868,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
           const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
 #pragma unroll
           for (int dt = 0; dt < NO; ++dt) {
-            const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + 16 * gg);
+            const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + vhalf);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               o[nb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[nb]), o[nb][dt], 0, 0, 0);
