@@ -112,8 +112,8 @@ def main():
                     help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the attention step shards by sequence or KV head with no exchange; see DESIGN.md).",
+        print("bench.py measures one GPU only: there is no multi-GPU path here "
+              "(the attention step would shard by sequence or by KV head, with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -73,6 +73,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_DEC_MIN_WAVES     // decode splits: the longest that still gives this many wavefronts
 #define CB_DEC_MIN_WAVES 8192
 #endif
+#ifndef CB_PF_REG_STAGES    // prefill K/V tiles in flight in registers (2: three-stage pipeline)
+#define CB_PF_REG_STAGES 2
+#endif
+#ifndef CB_PF_QK_AHEAD      // K fragment reads issued this far ahead of their QK MFMAs (0: compiler's order)
+#define CB_PF_QK_AHEAD 0
+#endif
+#ifndef CB_PF_PRIO          // wave priority raised around: 1 QK MFMAs, 2 QK and P V, 3 the softmax
+#define CB_PF_PRIO 1
+#endif
 #ifndef CB_NT_DECODE        // decode-only launch: K/V page loads with the non-temporal hint
 #define CB_NT_DECODE 1
 #endif
@@ -603,26 +612,30 @@ struct PfStage {            // one thread's share of one 64-key K/V tile
   uint4 v[N];
 };
 
+// Fetch the K half of tile ktk and the V half of tile ktv into registers.
 template <int D>
-__device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int* pids, int kt, int kt0,
-                                         int ctx, int kvh, int tid) {
+__device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int* pids, int ktk, int ktv,
+                                         int kt0, int kvh, int tid) {
   // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens.
   // Chunk i of a thread lies in page (tid + PF_THREADS i) / 2D of the tile,
-  // the same page for the whole wavefront; the tile's 4 page ids come from LDS
+  // the same page for the whole wavefront; a tile's 4 page ids come from LDS
   // in one read (-1 = no page).
-  const int4 ids = *reinterpret_cast<const int4*>(pids + (kt - kt0) * 4);
+  const int4 idk = *reinterpret_cast<const int4*>(pids + (ktk - kt0) * 4);
+  const int4 idv = *reinterpret_cast<const int4*>(pids + (ktv - kt0) * 4);
 #pragma unroll
   for (int i = 0; i < PfStage<D>::N; ++i) {
     const int e = tid + PF_THREADS * i;
     const int pgl = e / (2 * D), rem = e % (2 * D);
     // pages past the context (id -1) read page 0; their keys are masked by
-    // the causal test and their V tokens zeroed below (n <= 0)
-    const int id = pgl == 0 ? ids.x : pgl == 1 ? ids.y : pgl == 2 ? ids.z : ids.w;
-    const int ph = __builtin_amdgcn_readfirstlane(id);
-    const int phys = (unsigned)ph < (unsigned)p.num_pages ? ph : 0;
-    const size_t slab = (size_t)phys * p.hkv + kvh;
-    const uint8_t* kb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.k_cache + slab * 16 * D));
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.v_cache + slab * D * 16));
+    // the causal test and their V tokens zeroed when stored (n <= 0)
+    const int ik = pgl == 0 ? idk.x : pgl == 1 ? idk.y : pgl == 2 ? idk.z : idk.w;
+    const int iv = pgl == 0 ? idv.x : pgl == 1 ? idv.y : pgl == 2 ? idv.z : idv.w;
+    const int phk = __builtin_amdgcn_readfirstlane(ik);
+    const int phv = __builtin_amdgcn_readfirstlane(iv);
+    const size_t slk = (size_t)((unsigned)phk < (unsigned)p.num_pages ? phk : 0) * p.hkv + kvh;
+    const size_t slv = (size_t)((unsigned)phv < (unsigned)p.num_pages ? phv : 0) * p.hkv + kvh;
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.k_cache + slk * 16 * D));
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.v_cache + slv * D * 16));
     // the chunk's byte offset in both slabs: K row rem / (D/8), 8-dim chunk rem % (D/8);
     // V row rem / 2, 8-token half rem % 2.  Both are 16 rem bytes.  An unsigned
     // 32-bit offset from a uniform base lets the load take its scalar-base form.
@@ -633,18 +646,17 @@ __device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const 
   }
 }
 
-// Stage tile kt in LDS; V tokens at or past the context end, and below the
-// row tile's first key (`kfloor`: pages there may have been released), are
-// zeroed here, where the loaded data is consumed anyway.
+// Stage the registers' K half at kl and their V half (tile ktv) at vl.  V
+// tokens at or past the context end, and below the row tile's first key
+// (`kfloor`: pages there may have been released), are zeroed here, where the
+// loaded data is consumed anyway.
 template <int D, bool WIN>
-__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, int kt, int ctx, int kfloor,
-                                         int tid) {
+__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* kl, uint8_t* vl, int ktv, int ctx,
+                                         int kfloor, int tid) {
   using Lds = PfLds<D>;
-  uint8_t* kl = stage;
-  uint8_t* vl = stage + Lds::K_BYTES;
   // uniform: only the tile that holds the context end (or the window floor) masks
-  const bool tail = (kt + 1) * PF_KEYS > ctx;
-  const bool below = WIN && kt * PF_KEYS < kfloor;
+  const bool tail = (ktv + 1) * PF_KEYS > ctx;
+  const bool below = WIN && ktv * PF_KEYS < kfloor;
 #pragma unroll
   for (int i = 0; i < PfStage<D>::N; ++i) {
     const int e = tid + PF_THREADS * i;
@@ -656,7 +668,7 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* stage, i
     // (rows r and r + 8 are 256 bytes apart: same banks for the same half)
     uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + 16 * (hf ^ ((dr >> 3) & 1));
     uint4 vv = st.v[i];
-    const int k8 = (kt * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
+    const int k8 = (ktv * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
     const int n = ctx - k8;                          // valid tokens among these 8
     if (tail && n < 8) {
       vv.x = keep16(vv.x, 0, n);
@@ -757,8 +769,8 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   PfStage<D> sa, sb;
   const int klast = kt1 - 1;
   if (kt0 < kt1) {
-    pf_fetch<D>(sa, p, pids, kt0, kt0, ctx, kvh, tid);
-    pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), kt0, ctx, kvh, tid);
+    pf_fetch<D>(sa, p, pids, kt0, kt0, kt0, kvh, tid);
+    if (CB_PF_REG_STAGES == 2) pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), min(kt0 + 1, klast), kt0, kvh, tid);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -782,7 +794,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 
   uint8_t* stage0 = smem;
   uint8_t* stage1 = smem + Lds::STAGE;
-  if (kt0 < kt1) pf_store<D, WIN>(sa, stage0, kt0, ctx, kfloor, tid);
+  if (kt0 < kt1) pf_store<D, WIN>(sa, stage0, stage0 + Lds::K_BYTES, kt0, ctx, kfloor, tid);
   __syncthreads();
   auto tile_step = [&](int kt, const uint8_t* cur) {
     const int kbase = kt * PF_KEYS;
@@ -794,6 +806,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       // r = 0..15, key 16(r/8) + 8gg + r%8 of its subtile: the 8 consecutive
       // keys the P V product takes from it, with no exchange between lanes.
       floatx16 sc[NB][2];
+      if (CB_PF_PRIO == 1 || CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
@@ -808,6 +821,19 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
             sc[nb][sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[nb][cc], sc[nb][sub], 0, 0, 0);
         }
       }
+#if CB_PF_QK_AHEAD > 0
+      // the K fragment reads run CB_PF_QK_AHEAD ahead of the MFMAs that use
+      // them (the default schedule waits on each read right before its MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, CB_PF_QK_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NK - CB_PF_QK_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NB * CB_PF_QK_AHEAD, 0);
+#endif
+      if (CB_PF_PRIO == 1 || CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(0);
+      if (CB_PF_PRIO == 3) __builtin_amdgcn_s_setprio(1);
       // straddles this wave's diagonal (or the context end), or its window's lower edge
       if (kbase + PF_KEYS > w_kfull || (WIN && kbase < w_klo_max)) {
 #pragma unroll
@@ -848,6 +874,8 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       // for the same keys as one contiguous 16-byte load.  The row sum is
       // taken from the same bf16 P (a two-term dot product with ones per
       // packed pair), so the normaliser weighs exactly what P V does.
+      if (CB_PF_PRIO == 3) __builtin_amdgcn_s_setprio(0);
+      if (CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(1);
       float rsum[NB][2];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) rsum[nb][0] = rsum[nb][1] = 0.f;
@@ -874,21 +902,40 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
               o[nb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[nb]), o[nb][dt], 0, 0, 0);
           }
         }
+      if (CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) l[nb] += rsum[nb][0] + rsum[nb][1];
     }
   };
+#if CB_PF_REG_STAGES == 1
+  // two-stage pipeline: tile kt+1 loads into registers while tile kt is
+  // computed from LDS; stored into the other LDS stage after it
   for (int kt = kt0; kt < kt1; kt += 2) {
-    pf_fetch<D>(sa, p, pids, min(kt + 2, klast), kt0, ctx, kvh, tid);
+    const int k1 = min(kt + 1, klast), k2 = min(kt + 2, klast);
+    pf_fetch<D>(sb, p, pids, k1, k1, kt0, kvh, tid);
     tile_step(kt, stage0);
-    pf_store<D, WIN>(sb, stage1, min(kt + 1, klast), ctx, kfloor, tid);  // tile kt+1 (clamped)
+    pf_store<D, WIN>(sb, stage1, stage1 + Lds::K_BYTES, k1, ctx, kfloor, tid);
     __syncthreads();
     if (kt + 1 >= kt1) break;
-    pf_fetch<D>(sb, p, pids, min(kt + 3, klast), kt0, ctx, kvh, tid);
+    pf_fetch<D>(sb, p, pids, k2, k2, kt0, kvh, tid);
     tile_step(kt + 1, stage1);
-    pf_store<D, WIN>(sa, stage0, min(kt + 2, klast), ctx, kfloor, tid);  // tile kt+2 (clamped)
+    pf_store<D, WIN>(sb, stage0, stage0 + Lds::K_BYTES, k2, ctx, kfloor, tid);
     __syncthreads();
   }
+#else
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    const int k2 = min(kt + 2, klast), k1 = min(kt + 1, klast), k3 = min(kt + 3, klast);
+    pf_fetch<D>(sa, p, pids, k2, k2, kt0, kvh, tid);
+    tile_step(kt, stage0);
+    pf_store<D, WIN>(sb, stage1, stage1 + Lds::K_BYTES, k1, ctx, kfloor, tid);  // tile kt+1 (clamped)
+    __syncthreads();
+    if (kt + 1 >= kt1) break;
+    pf_fetch<D>(sb, p, pids, k3, k3, kt0, kvh, tid);
+    tile_step(kt + 1, stage1);
+    pf_store<D, WIN>(sa, stage0, stage0 + Lds::K_BYTES, k2, ctx, kfloor, tid);  // tile kt+2 (clamped)
+    __syncthreads();
+  }
+#endif
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {

@@ -20,7 +20,7 @@ is ``off = ctx - L`` and query row ``i`` sits at absolute position
     w_j    = exp(x_j - m)
     out    = sum_j w_j * v[j, g, :] / sum_j w_j
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
 * the causal boundary is inclusive (the page's mask keeps the diagonal:
   ``tril(diagonal=start)`` over absolute positions), so every query sees at
   least itself and no row is empty;

@@ -40,7 +40,7 @@ Follows these passages of the pages:
   a long prompt (the example: four prefills, at most one above 10,000
   tokens), so that short prompts need not wait behind a long one.
 
-Readings where the pages are silent or ambiguous (also listed in the design doc):
+Readings where the pages are silent or ambiguous:
 
 * chunk = min(remaining prompt, remaining token budget, ``max_prefill_chunk``
   when it is > 0); an active prefill is further cut to the tokens its held
