@@ -73,13 +73,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_DEC_MIN_WAVES     // decode splits: the longest that still gives this many wavefronts
 #define CB_DEC_MIN_WAVES 8192
 #endif
-#ifndef CB_PF_REG_STAGES    // prefill K/V tiles in flight in registers (2: three-stage pipeline)
-#define CB_PF_REG_STAGES 2
-#endif
-#ifndef CB_PF_QK_AHEAD      // K fragment reads issued this far ahead of their QK MFMAs (0: compiler's order)
-#define CB_PF_QK_AHEAD 0
-#endif
-#ifndef CB_PF_PRIO          // wave priority raised around: 1 QK MFMAs, 2 QK and P V, 3 the softmax
+#ifndef CB_PF_PRIO          // wave priority raised while the prefill QK MFMAs issue
 #define CB_PF_PRIO 1
 #endif
 #ifndef CB_NT_DECODE        // decode-only launch: K/V page loads with the non-temporal hint
@@ -106,13 +100,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_PF_THREADS
 #define CB_PF_THREADS 256
 #endif
-#ifndef CB_PF_NB           // 32-row blocks per prefill wave (2: one wave per SIMD)
-#define CB_PF_NB 1
-#endif
 constexpr int PF_THREADS = CB_PF_THREADS;   // threads of a prefill workgroup
 constexpr int PF_WAVES = PF_THREADS / 64;
-constexpr int PF_NB = CB_PF_NB;
-constexpr int PF_ROWS = PF_WAVES * 32 * PF_NB;  // query rows per prefill workgroup
+constexpr int PF_ROWS = PF_WAVES * 32;      // query rows per prefill workgroup (32 per wave)
 constexpr int PF_KEYS = 64;   // keys per prefill tile (4 pages)
 constexpr int PF_MAX_PAGES = 512;                          // page ids one prefill item stages in LDS
 constexpr int PF_MAX_KEYS = (PF_MAX_PAGES - 4) * 16 / PF_KEYS * PF_KEYS;  // largest key range per item
@@ -690,7 +680,6 @@ __device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* kl, uint
 template <int D, bool WIN>
 __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* smem) {
   using Lds = PfLds<D>;
-  constexpr int NB = PF_NB;   // 32-row blocks per wave: every K/V fragment read from LDS feeds NB MFMAs
   const int kvh = b % p.hkv;
   const int j = b / p.hkv;
   if (j >= p.pf_item_cap) return;
@@ -715,27 +704,20 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   const int vhalf = 16 * (gg ^ ((l32 >> 3) & 1));  // this lane's 16-byte half of a V row in LDS
   const int W = WIN ? p.window : 0;
 
-  // this lane's rows: block nb of the wave holds rows wave_base + 32 nb + l32
-  const int wave_base = tile * PF_ROWS + wv * 32 * NB;
-  int qi[NB], hh[NB], kcap[NB], kfirst[NB];
-  bool rvalid[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int row = wave_base + 32 * nb + l32;
-    rvalid[nb] = row < R;
-    qi[nb] = row / G;
-    hh[nb] = row - qi[nb] * G;
-    kcap[nb] = min(off + qi[nb], ctx - 1);             // last key this row may see
-    kfirst[nb] = window_first_key(off + qi[nb], W);    // first key this row may see
-  }
+  // this lane's row (GQA-packed: row = query token * G + head in the group)
+  const int row = tile * PF_ROWS + wv * 32 + l32;
+  const bool rvalid = row < R;
+  const int qi = row / G, hh = row - qi * G;
+  const int kcap = min(off + qi, ctx - 1);           // last key this row may see
+  const int kfirst = window_first_key(off + qi, W);  // first key this row may see
 
   // this item's key range, in whole 64-key tiles, from the tile's first row's window
   const int k_lo = (WIN ? tile_key_base(tile, G, off, W) : 0) + ks * p.pf_split_keys;
   const int k_hi = min(k_lo + p.pf_split_keys, tile_key_end(tile, L, G, ctx, off));
   const int kt0 = k_lo / PF_KEYS, kt1 = (k_hi + PF_KEYS - 1) / PF_KEYS;
   const int kfloor = window_first_key(off + tile * PF_ROWS / G, W);  // no row of the tile sees below
-  const int w_first_row = wave_base;
-  const int w_last_row = min(wave_base + 32 * NB - 1, R - 1);
+  const int w_first_row = tile * PF_ROWS + wv * 32;
+  const int w_last_row = min(w_first_row + 31, R - 1);
   const int w_kend = (w_first_row < R) ? min(ctx, off + w_last_row / G + 1) : 0;
   const int w_kfull = min(ctx, off + w_first_row / G + 1);  // keys below are visible to every row...
   const int w_klo_min = window_first_key(off + w_first_row / G, W);  // ...and at or above the window
@@ -758,38 +740,30 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   // The query fragments first: they are waited for once, here, while the
   // first two K/V tiles stay in flight (a load still pending at the loop
   // header would make the compiler wait inside the loop, draining the pipeline).
-  bf16x8 qf[NB][NK];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const uint16_t* qrow = p.q + ((size_t)(t0 + qi[nb]) * p.hq + kvh * G + hh[nb]) * D + 8 * gg;
+  bf16x8 qf[NK];
+  {
+    const uint16_t* qrow = p.q + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + 8 * gg;
 #pragma unroll
     for (int cc = 0; cc < NK; ++cc)
-      qf[nb][cc] = as_bf16x8(rvalid[nb] ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
+      qf[cc] = as_bf16x8(rvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
   }
   PfStage<D> sa, sb;
   const int klast = kt1 - 1;
   if (kt0 < kt1) {
     pf_fetch<D>(sa, p, pids, kt0, kt0, kt0, kvh, tid);
-    if (CB_PF_REG_STAGES == 2) pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), min(kt0 + 1, klast), kt0, kvh, tid);
+    pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), min(kt0 + 1, klast), kt0, kvh, tid);
   }
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int cc = 0; cc < NK; ++cc) {
-      const uint4 qq = __builtin_bit_cast(uint4, qf[nb][cc]);
-      asm volatile("" ::"v"(qq.x), "v"(qq.y), "v"(qq.z), "v"(qq.w));
-    }
-  floatx16 o[NB][NO];
-  float m[NB], l[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int dt = 0; dt < NO; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[nb][dt][r] = 0.f;
-    m[nb] = -INFINITY;
-    l[nb] = 0.f;
+  for (int cc = 0; cc < NK; ++cc) {
+    const uint4 qq = __builtin_bit_cast(uint4, qf[cc]);
+    asm volatile("" ::"v"(qq.x), "v"(qq.y), "v"(qq.z), "v"(qq.w));
   }
+  floatx16 o[NO];
+#pragma unroll
+  for (int dt = 0; dt < NO; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
   const float c = p.scale_log2;
 
   uint8_t* stage0 = smem;
@@ -805,124 +779,75 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       // (bits 2 and 3 of m swapped), so that lane (l32, gg) receives, for
       // r = 0..15, key 16(r/8) + 8gg + r%8 of its subtile: the 8 consecutive
       // keys the P V product takes from it, with no exchange between lanes.
-      floatx16 sc[NB][2];
-      if (CB_PF_PRIO == 1 || CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(1);
+      floatx16 sc[2];
+      if (CB_PF_PRIO) __builtin_amdgcn_s_setprio(1);  // the other wave's VALU work fills the MFMA gaps
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[nb][sub][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[sub][r] = 0.f;
 #pragma unroll
         for (int cc = 0; cc < NK; ++cc) {
           const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + krow) * Lds::KROW + (16 * cc + 8 * gg) * 2);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            sc[nb][sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[nb][cc], sc[nb][sub], 0, 0, 0);
+          sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[cc], sc[sub], 0, 0, 0);
         }
       }
-#if CB_PF_QK_AHEAD > 0
-      // the K fragment reads run CB_PF_QK_AHEAD ahead of the MFMAs that use
-      // them (the default schedule waits on each read right before its MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, CB_PF_QK_AHEAD, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * NK - CB_PF_QK_AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, NB * CB_PF_QK_AHEAD, 0);
-#endif
-      if (CB_PF_PRIO == 1 || CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(0);
-      if (CB_PF_PRIO == 3) __builtin_amdgcn_s_setprio(1);
+      if (CB_PF_PRIO) __builtin_amdgcn_s_setprio(0);
       // straddles this wave's diagonal (or the context end), or its window's lower edge
       if (kbase + PF_KEYS > w_kfull || (WIN && kbase < w_klo_max)) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kbase + sub * 32 + 16 * (r >> 3) + 8 * gg + (r & 7);
-              sc[nb][sub][r] = (key <= kcap[nb] && (!WIN || key >= kfirst[nb])) ? sc[nb][sub][r] : -INFINITY;
-            }
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mx = -INFINITY;
-#pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[nb][sub][r]);
-        mx = pair_max32(mx);
-        const bool raise = (mx - m[nb]) * c > CB_RESCALE_SLACK;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-          const float alpha = raise ? fast_exp2((m[nb] - mx) * c) : 1.f;
-          l[nb] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NO; ++dt) o[nb][dt] *= alpha;
-          m[nb] = raise ? mx : m[nb];
-        }
-        const float nm = neg_scaled(m[nb], c);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[nb][sub][r] = fast_exp2(fmaf(sc[nb][sub][r], c, nm));
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + sub * 32 + 16 * (r >> 3) + 8 * gg + (r & 7);
+            sc[sub][r] = (key <= kcap && (!WIN || key >= kfirst)) ? sc[sub][r] : -INFINITY;
+          }
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
+      mx = pair_max32(mx);
+      const bool raise = (mx - m) * c > CB_RESCALE_SLACK;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float alpha = raise ? fast_exp2((m - mx) * c) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NO; ++dt) o[dt] *= alpha;
+        m = raise ? mx : m;
+      }
+      const float nm = neg_scaled(m, c);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[sub][r] = fast_exp2(fmaf(sc[sub][r], c, nm));
 
       // O^T += V^T P^T, four 16-key steps (page 2*sub + half of the tile):
       // lane (l32, gg) holds P for keys 8gg..8gg+7 of the page, and reads V
       // for the same keys as one contiguous 16-byte load.  The row sum is
       // taken from the same bf16 P (a two-term dot product with ones per
       // packed pair), so the normaliser weighs exactly what P V does.
-      if (CB_PF_PRIO == 3) __builtin_amdgcn_s_setprio(0);
-      if (CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(1);
-      float rsum[NB][2];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) rsum[nb][0] = rsum[nb][1] = 0.f;
+      float rsum[2] = {0.f, 0.f};
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int r0 = 8 * half;
-          uint4 pb[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            pb[nb] = make_uint4(pack_bf16x2(sc[nb][sub][r0 + 0], sc[nb][sub][r0 + 1]),
-                                pack_bf16x2(sc[nb][sub][r0 + 2], sc[nb][sub][r0 + 3]),
-                                pack_bf16x2(sc[nb][sub][r0 + 4], sc[nb][sub][r0 + 5]),
-                                pack_bf16x2(sc[nb][sub][r0 + 6], sc[nb][sub][r0 + 7]));
-            rsum[nb][half] = sum_bf16x8(pb[nb], rsum[nb][half]);
-          }
+          const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
+                                      pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
+                                      pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
+                                      pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
+          rsum[half] = sum_bf16x8(pb, rsum[half]);
           const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
 #pragma unroll
           for (int dt = 0; dt < NO; ++dt) {
             const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + vhalf);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              o[nb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[nb]), o[nb][dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
           }
         }
-      if (CB_PF_PRIO == 2) __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) l[nb] += rsum[nb][0] + rsum[nb][1];
+      l += rsum[0] + rsum[1];
     }
   };
-#if CB_PF_REG_STAGES == 1
-  // two-stage pipeline: tile kt+1 loads into registers while tile kt is
-  // computed from LDS; stored into the other LDS stage after it
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    const int k1 = min(kt + 1, klast), k2 = min(kt + 2, klast);
-    pf_fetch<D>(sb, p, pids, k1, k1, kt0, kvh, tid);
-    tile_step(kt, stage0);
-    pf_store<D, WIN>(sb, stage1, stage1 + Lds::K_BYTES, k1, ctx, kfloor, tid);
-    __syncthreads();
-    if (kt + 1 >= kt1) break;
-    pf_fetch<D>(sb, p, pids, k2, k2, kt0, kvh, tid);
-    tile_step(kt + 1, stage1);
-    pf_store<D, WIN>(sb, stage0, stage0 + Lds::K_BYTES, k2, ctx, kfloor, tid);
-    __syncthreads();
-  }
-#else
   for (int kt = kt0; kt < kt1; kt += 2) {
     const int k2 = min(kt + 2, klast), k1 = min(kt + 1, klast), k3 = min(kt + 3, klast);
     pf_fetch<D>(sa, p, pids, k2, k2, kt0, kvh, tid);
@@ -935,34 +860,30 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     pf_store<D, WIN>(sa, stage0, stage0 + Lds::K_BYTES, k2, ctx, kfloor, tid);  // tile kt+2 (clamped)
     __syncthreads();
   }
-#endif
 
+  const float lt = pair_sum32(l);
+  if (!rvalid) return;
+  if (nsplit == 1) {
+    const float inv = 1.f / lt;
+    uint16_t* orow = p.out + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float lt = pair_sum32(l[nb]);
-    if (!rvalid[nb]) continue;
-    if (nsplit == 1) {
-      const float inv = 1.f / lt;
-      uint16_t* orow = p.out + ((size_t)(t0 + qi[nb]) * p.hq + kvh * G + hh[nb]) * D;
+    for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NO; ++dt)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint2 v = make_uint2(pack_bf16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv),
+                                   pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv));
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
+      }
+  } else {
+    const size_t prow = ((size_t)slot * p.hkv + kvh) * PF_ROWS + wv * 32 + l32;
+    float* po = p.pf_o + prow * D;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint2 v = make_uint2(pack_bf16x2(o[nb][dt][4 * q4 + 0] * inv, o[nb][dt][4 * q4 + 1] * inv),
-                                     pack_bf16x2(o[nb][dt][4 * q4 + 2] * inv, o[nb][dt][4 * q4 + 3] * inv));
-          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * gg) = v;
-        }
-    } else {
-      const size_t prow = ((size_t)slot * p.hkv + kvh) * PF_ROWS + wv * 32 * NB + 32 * nb + l32;
-      float* po = p.pf_o + prow * D;
+    for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NO; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<floatx4*>(po + 32 * dt + 8 * q4 + 4 * gg) =
-              floatx4{o[nb][dt][4 * q4 + 0], o[nb][dt][4 * q4 + 1], o[nb][dt][4 * q4 + 2], o[nb][dt][4 * q4 + 3]};
-      if (gg == 0) p.pf_ml[prow] = make_float2(m[nb], lt);
-    }
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<floatx4*>(po + 32 * dt + 8 * q4 + 4 * gg) =
+            floatx4{o[dt][4 * q4 + 0], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+    if (gg == 0) p.pf_ml[prow] = make_float2(m, lt);
   }
 }
 
@@ -972,7 +893,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 // LDS nor the prefill registers and runs at higher occupancy.
 // ---------------------------------------------------------------------------
 template <int D, bool WIN>
-__global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS / PF_NB) void attn_mixed_kernel(Params p) {
+__global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
   const int b = blockIdx.x;
   const int np = p.pf_blocks, nd = (int)gridDim.x - np;
