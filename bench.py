@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import subprocess
 import math
 import os
 import sys
@@ -108,6 +109,10 @@ def main():
                     help="physical page ids: a seeded random permutation (default) or handed out in order")
     ap.add_argument("--graphs", default="",
                     help="Q,KV padding intervals: replay each padded step shape from a recorded HIP graph")
+    ap.add_argument("--cold", default="auto", choices=["auto", "on", "off"],
+                    help="write a 1 GiB scratch buffer before every timed step so that no cache level holds "
+                         "the step's data (auto: on when the step moves less than 1 GB); the step time is then "
+                         "the device span of each step")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
     args = ap.parse_args()
@@ -173,6 +178,8 @@ def main():
     esize = 2 if w.dtype == "bf16" else 4
     bytes_alg, flops_alg, pairs = algorithmic(desc0, hq, hkv, d, esize, args.window)
     lib = cb.load()
+    cold = args.cold == "on" or (args.cold == "auto" and bytes_alg < 1e9)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold else None
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     stops = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     span0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -182,6 +189,9 @@ def main():
     stream = layer.graph_stream if layer.graphs else torch.cuda.current_stream(dev)
 
     def one_step(k=None):
+        if cold:                                               # evict the step's data from L2 and MALL
+            with torch.cuda.stream(stream):
+                scratch.fill_(k or 0)
         layer.load_builder(snapshot)                           # same starting state each time
         layer.schedule(stream=stream)                          # a1 + a2
         if layer.graphs:                                       # events around the whole graph
@@ -212,9 +222,12 @@ def main():
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, stops)]
     kern_s = float(np.mean(kern_ms)) / 1e3
     if layer.graphs:      # the graph's events already span append .. combine
-        span_s = kern_s
+        span_ms = kern_ms
     else:
-        span_s = float(np.mean([s.elapsed_time(e) for s, e in zip(span0, span1)])) / 1e3
+        span_ms = [s.elapsed_time(e) for s, e in zip(span0, span1)]
+    span_s = float(np.mean(span_ms)) / 1e3
+    if cold:              # the wall clock includes the flushes: a step is its device span
+        step_s = span_s
     assert torch.isfinite(out[:T].float()).all(), "non-finite attention output"
 
     t_hbm, t_mfma = bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)
@@ -235,6 +248,15 @@ def main():
     roof["kernel_us"] = round(kern_s * 1e6, 2)
     roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
     roof["device_span_us"] = round(span_s * 1e6, 2)   # kv_append .. combine on the device
+    pct = lambda xs, q: round(float(np.percentile(xs, q)) * 1e3, 2)
+    roof["kernel_us_p10_p50_p90"] = [pct(kern_ms, 10), pct(kern_ms, 50), pct(kern_ms, 90)]
+    roof["span_us_p10_p50_p90"] = [pct(span_ms, 10), pct(span_ms, 50), pct(span_ms, 90)]
+    roof["timing"] = ("cold: 1 GiB written before each step; step = device span" if cold
+                      else "warm: steps back to back; step = wall time")
+    if roof["bound"] == "hbm":   # beside the peak: a plain streaming read of as many bytes
+        ach = achievable_read_gbs(max(bytes_alg, 1 << 30))
+        roof["achievable_read_GBps"] = ach
+        roof["frac_of_achievable"] = round(roof["achieved"] / ach, 4) if ach else None
     log(f"[bench] host enqueue {(t_enq - t0) / args.steps * 1e3:.3f} ms/step")
     log(f"[bench] device span (append .. combine) {span_s * 1e6:.1f} us")
     log(f"[bench] step {step_s * 1e3:.3f} ms, attention kernel {kern_s * 1e6:.1f} us, "
@@ -258,6 +280,19 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def achievable_read_gbs(nbytes):
+    """GB/s of the streaming-read probe (a child process) over ``nbytes``, or None."""
+    probe = os.path.join(ROOT, "chunked_prefill_attention_amd", "hbm_probe")
+    if not os.path.exists(probe):
+        return None
+    nbytes = (int(nbytes) + (1 << 20) - 1) >> 20 << 20
+    try:
+        r = subprocess.run([probe, "read", str(nbytes), "10"], capture_output=True, text=True, timeout=120)
+        return float(json.loads(r.stdout.strip().splitlines()[-1])["GBps"]) if r.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, KeyError, IndexError):
+        return None
 
 
 def cpu_baseline(desc, q, hist, hq, hkv, d, budget_s, gpu_out, window=0):
