@@ -1126,16 +1126,24 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
 
 }  // namespace
 
-// Compute units of the current device (cached per device; 256 if unknown).
-static int device_cus() {
-  static std::atomic<int> cache[64];
+// Workgroups of the mixed launch the current device holds at once: the
+// kernel's occupancy per CU (LDS and registers; 2 for D 128) times the CU
+// count.  Cached per device and head size; 512 when there is no device.
+static int mixed_slots(int head_dim) {
+  static std::atomic<int> cache[64][2];
+  const int hd = head_dim == 64 ? 1 : 0;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  cache[dev].store(n, std::memory_order_relaxed);
-  return n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  int v = cache[dev][hd].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  const void* f = hd ? reinterpret_cast<const void*>(&attn_mixed_kernel<64, false>)
+                     : reinterpret_cast<const void*>(&attn_mixed_kernel<128, false>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, PF_THREADS, 0) != hipSuccess || per <= 0) per = 2;
+  v = cus * per;
+  cache[dev][hd].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq, int32_t hkv,
@@ -1165,7 +1173,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
   pl.pf_may_split = max_splits > 1;
   pl.hkv = hkv;
-  pl.slots = 2 * device_cus();  // two prefill-sized workgroups per CU (LDS bound)
+  pl.slots = mixed_slots(head_dim);
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 0;
   pl.off_hdr = off;         off = align(off + 16);
