@@ -1091,7 +1091,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
   const int64_t dec_blocks = (pl.dec_cap * a.hkv + PF_WAVES - 1) / PF_WAVES;
   p.pf_blocks = (int32_t)pf_blocks;
-  p.slots = pl.slots;
+  p.slots = pl.slots > 0 ? pl.slots : mixed_slots(D);
   const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
   const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
   const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv * (PF_ROWS / CP_ROWS) : 0;
@@ -1129,7 +1129,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
 // Workgroups of the mixed launch the current device holds at once: the
 // kernel's occupancy per CU (LDS and registers; 2 for D 128) times the CU
 // count.  Cached per device and head size; 512 when there is no device.
-static int mixed_slots(int head_dim) {
+int mixed_slots(int head_dim) {
   static std::atomic<int> cache[64][2];
   const int hd = head_dim == 64 ? 1 : 0;
   int dev = 0;
@@ -1173,7 +1173,6 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
   pl.pf_may_split = max_splits > 1;
   pl.hkv = hkv;
-  pl.slots = mixed_slots(head_dim);
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 0;
   pl.off_hdr = off;         off = align(off + 16);

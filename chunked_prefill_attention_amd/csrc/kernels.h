@@ -49,11 +49,15 @@ struct Bf16Plan {
   int64_t pf_tile_cap;    // bound on (sequence, 128-row tile) prefill tiles
   int64_t pf_item_cap;    // bound on (tile, key split) prefill items
   int32_t hkv;            // KV heads (workgroups per prefill item)
-  int32_t slots;          // workgroups of the mixed launch the device holds at once
+  int32_t slots;          // workgroups of the mixed launch the device holds at once (0: ask the
+                          // device at launch; the host list builder needs it set, see mixed_slots)
   size_t off_hdr, off_dec_items, off_pf_items, off_pf_tiles, off_dec_first, off_dec_rem;
   size_t off_dec_ml, off_dec_o, off_pf_ml, off_pf_o;
   size_t bytes;
 };
+// Workgroups of the mixed launch the current device holds at once (its
+// occupancy per CU times the CU count; queried once per device and head size).
+int mixed_slots(int head_dim);
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
                    int32_t hkv, int32_t head_dim, int32_t max_context_len);
 
