@@ -1,0 +1,44 @@
+"""bench.py's output contract: one JSON line with the metric, throughput,
+roofline and CPU-baseline fields, and a clear refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench(*args, timeout=600):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True,
+                          text=True, timeout=timeout, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _bench("--gpus", "2", timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_json_line_fields():
+    r = _bench("--steps", "3", "--warmup", "1", "--cpu-seconds", "0.2")
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    rec = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
+    assert rec["value"] > 0 and rec["ms_per_step"] > 0 and rec["higher_is_better"] is True
+    assert rec["dtype"] == "bf16" and rec["config"]["workload"]
+    roof = rec["roofline"]
+    assert roof["bound"] in ("hbm", "mfma") and roof["unit"] in ("GB/s", "TFLOP/s")
+    assert 0 < roof["frac"] <= 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert roof["traffic"] is None or roof["traffic"] > 0
+    cpu = rec["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    # the oracle's rows agree with the GPU's within the bf16 bound the parity tests use
+    assert cpu["max_abs_err_vs_gpu"] < 0.05
