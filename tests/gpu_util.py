@@ -133,9 +133,10 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "", absmea
     kernel's arithmetic when ``absmean`` (attention over |V|) is given.
 
     Derived bound: the probabilities enter the P V product rounded to bf16
-    (relative error <= 2^-9 each) while the normaliser keeps them in fp32, so
-    the pre-rounding output error is at most 2 * 2^-9 * sum_j w_j |v_j| / sum_j w_j;
-    the final rounding to bf16 adds 2^-9 |out|.  The check allows twice that.
+    (relative error <= 2^-9 each); the normaliser sums them in fp32 (decode)
+    or sums the same rounded values (prefill).  Either way the pre-rounding
+    output error is at most 2 * 2^-9 * sum_j w_j |v_j| / sum_j w_j; the final
+    rounding to bf16 adds 2^-9 |out|.  The check allows twice that.
     """
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"

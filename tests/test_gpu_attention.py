@@ -261,3 +261,33 @@ def test_engine_mixed_bf16_matches_direct_calls_bitwise():
                                wl.softmax_scale(d))
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), step
+
+
+def test_interleaved_block_order_matches_oracle():
+    """More live prefill workgroups than the device holds at once, beside
+    decodes: the mixed launch alternates prefill and decode blocks.  The work
+    lists' header (at the front of the workspace) records the order used."""
+    seqs = [(300 + 97 * i, 1) for i in range(8)] + [(8048, 2048)]
+    hq, hkv, d = 32, 8, 128
+    say("interleaved block order: 8 decodes + 2048 tokens at offset 6000")
+    st = Step(seqs, hq, hkv, d, "bf16", seed=11)
+    kc, vc = st.upload()
+    ws = torch.empty(cb.attention_workspace_bytes(len(seqs), st.num_decodes, st.T, hq, hkv, d, st.max_ctx, 1),
+                     dtype=torch.uint8, device=kc.device)
+    q = to_dev(np.concatenate(st.q), "bf16")
+    out = cb.attention_step(q, kc, vc, i32(st.bt), i32(st.qsl), i32(st.ctx), i32(st.off), st.num_decodes,
+                            st.max_ctx, st.scale, workspace=ws)
+    torch.cuda.synchronize()
+    live_pf, live_dec, order = (int(x) for x in ws[:16].view(torch.int32).cpu()[:3])
+    assert live_dec > 0 and live_pf * hkv > 512 and order == 1, (live_pf, live_dec, order)
+    worst = 0.0
+    for s in range(st.num_decodes):
+        ref = ora.attend(st.q[s], st.k_hist[s], st.v_hist[s], st.scale)
+        worst = max(worst, compare(st.out_rows(out, s), ref, "bf16", f"decode {s}"))
+    s = len(seqs) - 1
+    pick = sorted(set([0, 1, 1023, 2046, 2047] + wl.uniform_ints(5, 8, 0, 2047).tolist()))
+    rows = [(i, h) for i in pick for h in range(hq)]
+    ref = ora.attend_rows(st.q[s], st.k_hist[s], st.v_hist[s], st.scale, rows=rows)
+    am = ora.attend_rows(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale, rows=rows)
+    worst = max(worst, compare(st.out_rows(out, s)[pick], ref[pick], "bf16", "prefill rows", am[pick]))
+    say(f"  live prefill items {live_pf}, decode items {live_dec}; max abs err {worst:.2e}")
