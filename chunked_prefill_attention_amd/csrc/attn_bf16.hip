@@ -133,7 +133,8 @@ struct Params {
   int32_t num_pages;
   int32_t split_pages;   // pages per decode item
   int32_t pf_split_keys; // keys per prefill item (multiple of PF_KEYS)
-  int32_t pf_blocks;     // grid blocks reserved for prefill items
+  int32_t pf_blocks;     // prefill workgroups the work lists can hold
+  int32_t dec_blocks;    // decode workgroups (PF_WAVES wavefronts) the work lists can hold
   int32_t slots;         // workgroups of the mixed launch the device holds at once
   int32_t dec_cap, pf_tile_cap, pf_item_cap;
   int32_t comb_dec_blocks;
@@ -896,9 +897,9 @@ template <int D, bool WIN>
 __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
   const int b = blockIdx.x;
-  const int np = p.pf_blocks, nd = (int)gridDim.x - np;
-  // live blocks first, in the order the header names; the blocks the caps
-  // reserve beyond the live work (they find no item and return) come last
+  const int np = p.pf_blocks, nd = p.dec_blocks;
+  // live blocks first, in the order the header names; a grid sized by the
+  // caps has blocks past the live work, which return at once
   const int4 h = *p.hdr;
   const int lp = min(h.x * p.hkv, np);
   const int ld = min((h.y * p.hkv + PF_WAVES - 1) / PF_WAVES, nd);
@@ -917,9 +918,7 @@ __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kerne
       else dec = m8 + r - (lp - m8);
     }
   } else {
-    const int r = b - lp - ld;
-    if (r < np - lp) pf = lp + r;
-    else dec = ld + r - (np - lp);
+    return;  // past the live work (the grid is sized by the caps): nothing to do
   }
   if (pf >= 0) {
     prefill_tile<D, WIN>(p, pf, smem);
@@ -1091,6 +1090,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
   const int64_t dec_blocks = (pl.dec_cap * a.hkv + PF_WAVES - 1) / PF_WAVES;
   p.pf_blocks = (int32_t)pf_blocks;
+  p.dec_blocks = (int32_t)dec_blocks;
   p.slots = pl.slots > 0 ? pl.slots : mixed_slots(D);
   const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
   const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
@@ -1110,11 +1110,17 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
   const bool win = a.window > 0;
   if (pf_blocks > 0) {
-    const dim3 grid((unsigned)(pf_blocks + dec_blocks));
+    int64_t nblk = pf_blocks + dec_blocks;
+    if (lists && lists->live_pf_items >= 0 && lists->live_dec_items >= 0)
+      nblk = std::min<int64_t>(pf_blocks, lists->live_pf_items * a.hkv) +
+             std::min<int64_t>(dec_blocks, (lists->live_dec_items * a.hkv + PF_WAVES - 1) / PF_WAVES);
+    const dim3 grid((unsigned)std::max<int64_t>(nblk, 1));
     if (win) hipLaunchKernelGGL((attn_mixed_kernel<D, true>), grid, dim3(PF_THREADS), 0, stream, p);
     else hipLaunchKernelGGL((attn_mixed_kernel<D, false>), grid, dim3(PF_THREADS), 0, stream, p);
   } else if (dec_blocks > 0) {
-    const dim3 grid((unsigned)((pl.dec_cap * a.hkv + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64)));
+    int64_t waves = pl.dec_cap * a.hkv;
+    if (lists && lists->live_dec_items >= 0) waves = std::min<int64_t>(waves, lists->live_dec_items * a.hkv);
+    const dim3 grid((unsigned)std::max<int64_t>((waves + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64), 1));
     if (win) hipLaunchKernelGGL((attn_decode_kernel<D, true>), grid, dim3(CB_DEC_WG), 0, stream, p);
     else hipLaunchKernelGGL((attn_decode_kernel<D, false>), grid, dim3(CB_DEC_WG), 0, stream, p);
   }
@@ -1215,7 +1221,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
 // Mirrors plan_kernel: decode items longest first (every full split, then the
 // short last splits by decreasing length, sequences in order within a
 // length), prefill tiles heaviest (last) first with their key splits.
-void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G, int32_t window,
+WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G, int32_t window,
                       const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst) {
   const WorkListLayout L = work_list_layout(pl, num_decodes);
   uint8_t* base = static_cast<uint8_t*>(dst);
@@ -1281,6 +1287,7 @@ void build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes,
   const int64_t pl_live = std::min<int64_t>(ni, pl.pf_item_cap), dl_live = std::min<int64_t>(n, pl.dec_cap);
   *reinterpret_cast<int4*>(base + L.hdr) =
       make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), 0);
+  return WorkCounts{pl_live, dl_live};
 }
 
 }  // namespace cb

@@ -236,7 +236,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     const cb::WorkListLayout lay = cb::work_list_layout(pl, e->x_ndec);
     const size_t at = (off + 3) & ~size_t(3);  // 16-byte aligned (int32 units)
     if ((int64_t)(at + lay.bytes / 4) <= e->slot_ints) {
-      cb::build_work_lists(pl, e->x_nseq, e->x_ndec, e->cfg.num_q_heads / e->cfg.num_kv_heads,
+      const cb::WorkCounts live = cb::build_work_lists(pl, e->x_nseq, e->x_ndec, e->cfg.num_q_heads / e->cfg.num_kv_heads,
                            e->cfg.builder.sliding_window, h + o_qsl, h + o_ctx, h + o_off, h + at);
       const uint8_t* db = reinterpret_cast<const uint8_t*>(dv + at);
       e->lists.hdr = db + lay.hdr;
@@ -245,6 +245,9 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
       e->lists.pf_tiles = db + lay.pf_tiles;
       e->lists.dec_first = reinterpret_cast<const int32_t*>(db + lay.dec_first);
       e->lists.dec_rem = reinterpret_cast<const int32_t*>(db + lay.dec_rem);
+      // a recorded graph keeps its grid for every replay: it is sized by the caps
+      e->lists.live_pf_items = e->capture ? -1 : live.pf_items;
+      e->lists.live_dec_items = e->capture ? -1 : live.dec_items;
       e->have_lists = true;
       off = at + lay.bytes / 4;
     }
