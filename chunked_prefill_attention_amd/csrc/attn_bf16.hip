@@ -19,16 +19,21 @@
 //  * prefill item = one 256-thread workgroup on (sequence, KV head, tile of
 //    128 query rows, range of keys), where a row is a (query token, query
 //    head of the group) pair so the G heads sharing a KV head read K/V once.
-//    Per 64-key tile the workgroup stages K and V pages in LDS (double
-//    buffered: the next tile's global loads are in flight while the current
-//    tile is computed); each wavefront computes S^T = K Q^T for its 32 rows
-//    with 32x32x16 bf16 MFMAs, masks only the tiles that straddle its
+//    Per 64-key tile the workgroup stages K and V pages in LDS through a
+//    three-stage pipeline (tile k+2 loading into registers, k+1 in the second
+//    LDS stage, k computed); each wavefront computes S^T = K Q^T for its 32
+//    rows with 32x32x16 bf16 MFMAs, masks only the tiles that straddle its
 //    diagonal, updates the online softmax and accumulates O^T = V^T P^T.
 //    Tiles wholly above the diagonal are never loaded.  Long key ranges are
 //    cut into several items so that a long chunk spreads over every CU.
 //
 // Items with more than one split write unnormalised partial results (row
 // max, row sum, O); the combine kernel merges them by log-sum-exp.
+//
+// Block order: the work lists start with the live item counts; live blocks
+// run first (prefill first when its workgroups fit in one round of the
+// device's slots, else prefill and decode alternating) and blocks past the
+// live work return at once.
 //
 // Layouts: K pages are token-major ([16][D] per (page, head)), so a lane's
 // MFMA A-operand (one key, 8 consecutive dims) is one 16-byte load.  V pages
@@ -38,11 +43,11 @@
 //
 // Numerics: bf16 inputs, fp32 MFMA accumulation, softmax in fp32 (scores kept
 // in raw units; exponentials are exp2(s*scale*log2(e) - m*scale*log2(e)) with
-// one FMA), probabilities rounded to bf16 for the P V product, output
-// rounded to bf16 (round to nearest even).  The running max is raised only
-// when a score exceeds it by more than 2^3 in exponent units, so the
-// accumulator rescale is usually skipped; weights stay <= 2^8, exact in the
-// normalisation.  Cache slots at or past the context length are masked by
+// one FMA), probabilities rounded to bf16 for the P V product (and, in
+// prefill, for the row sum, so numerator and normaliser weigh the same
+// values), output rounded to bf16 (round to nearest even).  The running max
+// is raised only when a score exceeds it by more than 8 in log2 units, so
+// the accumulator rescale is usually skipped; weights stay <= 2^8.  Cache slots at or past the context length are masked by
 // select and their V entries zeroed, so garbage or NaN there never reaches
 // the output.
 #include <hip/hip_runtime.h>
