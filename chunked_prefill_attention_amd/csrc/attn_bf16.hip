@@ -19,11 +19,13 @@
 //  * prefill item = one 256-thread workgroup on (sequence, KV head, tile of
 //    128 query rows, range of keys), where a row is a (query token, query
 //    head of the group) pair so the G heads sharing a KV head read K/V once.
-//    Per 64-key tile the workgroup stages K and V pages in LDS through a
-//    three-stage pipeline (tile k+2 loading into registers, k+1 in the second
-//    LDS stage, k computed); each wavefront computes S^T = K Q^T for its 32
-//    rows with 32x32x16 bf16 MFMAs, masks only the tiles that straddle its
-//    diagonal, updates the online softmax and accumulates O^T = V^T P^T.
+//    Per 64-key tile the workgroup copies K and V pages straight from the
+//    cache into LDS (global_load_lds, each wavefront one page; tile k+1 is
+//    copied into one LDS stage while tile k is computed from the other);
+//    each wavefront computes S^T = K Q^T for its 32 rows with 32x32x16 bf16
+//    MFMAs, reading its K and V fragments from LDS in batches ahead of the
+//    MFMAs, masks only the tiles that straddle its diagonal, updates the
+//    online softmax and accumulates O^T = V^T P^T.
 //    Tiles wholly above the diagonal are never loaded.  Long key ranges are
 //    cut into several items so that a long chunk spreads over every CU.
 //
@@ -48,10 +50,11 @@
 // values), output rounded to bf16 (round to nearest even).  The running max
 // is raised only when a score exceeds it by more than 8 in log2 units, so
 // the accumulator rescale is usually skipped; weights stay <= 2^8.  Cache slots at or past the context length are masked by
-// select and their V entries zeroed, so garbage or NaN there never reaches
-// the output.
+// select and their V entries zeroed (in prefill, as they are read from LDS),
+// so garbage or NaN there never reaches the output.
 #include <hip/hip_runtime.h>
 #include <atomic>
+#include <type_traits>
 #include <vector>
 
 #include <algorithm>
@@ -84,8 +87,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_NT_DECODE        // decode-only launch: K/V page loads with the non-temporal hint
 #define CB_NT_DECODE 1
 #endif
-#ifndef CB_NT_PREFILL       // prefill K/V tile loads with the non-temporal hint (tiles are re-read)
-#define CB_NT_PREFILL 0
+#ifndef CB_PF_READAHEAD     // prefill: K and V fragments read from LDS in batches of this many (0: compiler's order)
+#define CB_PF_READAHEAD 4
 #endif
 // threads per workgroup of the decode-only kernel (64 or 256)
 #ifndef CB_DEC_WG
@@ -149,13 +152,12 @@ struct Params {
 
 template <int D>
 struct PfLds {
-  static constexpr int KROW = D * 2 + 16;  // padded K row (bytes) in LDS
+  static constexpr int KROW = D * 2;       // K row (bytes) in LDS, 16-byte chunks swizzled by row
   static constexpr int VROW = 32;          // (page, dim) row of 16 tokens (bytes), halves swapped on rows with bit 3 set
   static constexpr int K_BYTES = PF_KEYS * KROW;
   static constexpr int V_BYTES = (PF_KEYS / 16) * D * VROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int BYTES = 2 * STAGE;  // double buffered
-  static constexpr int TOTAL = BYTES + PF_MAX_PAGES * 4;  // + the item's page ids
+  static constexpr int STAGE = K_BYTES + V_BYTES;  // one tile; two stages, then the item's page ids
+  static_assert(2 * STAGE <= 65536, "copy destinations (M0) below 64 KB");
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -601,90 +603,105 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
 // ---------------------------------------------------------------------------
 // Prefill: one workgroup per (sequence, KV head, 128-row tile, key split).
 // ---------------------------------------------------------------------------
+// Direct copy of K/V tiles into LDS (global_load_lds_dwordx4: lane i of a
+// wave's load writes 16 bytes at the LDS address in M0 plus 16 i, from any
+// address of its own).  Each wave copies one page of a tile, K and V, in 1 KB
+// loads; the per-lane source offsets are fixed, so a tile costs a wave one
+// page address.  The immediate offset advances the source and the LDS
+// destination together.
+//
+// K rows are stored unpadded with their 16-byte chunks permuted: logical chunk
+// c of tile row r sits at chunk c ^ kswz(r), so the 16 rows that one chunk
+// read of 16 lanes touches fall on 16 different 16-byte bank groups.
 template <int D>
-struct PfStage {            // one thread's share of one 64-key K/V tile
-  static constexpr int N = 8 * D / PF_THREADS;  // 16-byte chunks of K (and of V) per thread
-  uint4 k[N];
-  uint4 v[N];
+__host__ __device__ constexpr int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
+template <int J>
+__device__ __forceinline__ void lds_copy16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), reinterpret_cast<void*>(dst), 16, J * 1024, 0);
+}
+
+// Source offsets, per lane, of the NJ 1 KB loads that fill one page of K
+// (each less the load's immediate offset J * 1 KB), and of the loads of one
+// page of V (the same for every J: V rows of 32 bytes, halves swapped on rows
+// with bit 3 set, as the P V reads expect).
+template <int D>
+struct PfDmaOffsets {
+  static constexpr int NJ = D / 32;  // 1 KB loads per page slab (16 x D bf16)
+  uint32_t k[NJ];
+  uint32_t v;
+  __device__ __forceinline__ explicit PfDmaOffsets(int lane) {
+    constexpr int CPR = D / 8;           // 16-byte chunks per K row
+    constexpr int RPL = 1024 / (2 * D);  // K rows per 1 KB load
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int rl = RPL * j + lane / CPR;  // page row this lane fills
+      const int c = (lane % CPR) ^ kswz<D>(rl);
+      k[j] = (uint32_t)((lane / CPR) * 2 * D + 16 * c);
+    }
+    v = (uint32_t)((lane >> 1) * 32 + 16 * ((lane & 1) ^ ((lane >> 4) & 1)));
+  }
 };
 
-// Fetch the K half of tile ktk and the V half of tile ktv into registers.
+// Wave w copies page w of tile kt (K and V) into the LDS stage at `st`.
+// Pages past the context (id -1) read page 0; their keys are masked and
+// their V tokens zeroed where they are read.
 template <int D>
-__device__ __forceinline__ void pf_fetch(PfStage<D>& st, const Params& p, const int* pids, int ktk, int ktv,
-                                         int kt0, int kvh, int tid) {
-  // K: 4 pages x 16 rows x D bf16 in 16-byte chunks; V: 4 pages x D rows x 16 tokens.
-  // Chunk i of a thread lies in page (tid + PF_THREADS i) / 2D of the tile,
-  // the same page for the whole wavefront; a tile's 4 page ids come from LDS
-  // in one read (-1 = no page).
-  const int4 idk = *reinterpret_cast<const int4*>(pids + (ktk - kt0) * 4);
-  const int4 idv = *reinterpret_cast<const int4*>(pids + (ktv - kt0) * 4);
+__device__ __forceinline__ void pf_dma(uint8_t* st, const Params& p, const int* pids, int kt, int kt0, int kvh, int w,
+                                       const PfDmaOffsets<D>& od) {
+  constexpr int SLAB = 32 * D;  // bytes of one page of one KV head, K or V
+  const int id = __builtin_amdgcn_readfirstlane(pids[(kt - kt0) * 4 + w]);
+  const size_t slab = (size_t)((unsigned)id < (unsigned)p.num_pages ? id : 0) * p.hkv + kvh;
+  const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.k_cache) + slab * SLAB;
+  const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.v_cache) + slab * SLAB;
+  uint8_t* kl = st + w * SLAB;
+  uint8_t* vl = st + PfLds<D>::K_BYTES + w * SLAB;
+  // unsigned 32-bit offsets from a uniform base: the loads take their
+  // scalar-base form (the empty asm keeps each offset 32-bit at its load)
+  uint32_t o[PfDmaOffsets<D>::NJ + 1];
 #pragma unroll
-  for (int i = 0; i < PfStage<D>::N; ++i) {
-    const int e = tid + PF_THREADS * i;
-    const int pgl = e / (2 * D), rem = e % (2 * D);
-    // pages past the context (id -1) read page 0; their keys are masked by
-    // the causal test and their V tokens zeroed when stored (n <= 0)
-    const int ik = pgl == 0 ? idk.x : pgl == 1 ? idk.y : pgl == 2 ? idk.z : idk.w;
-    const int iv = pgl == 0 ? idv.x : pgl == 1 ? idv.y : pgl == 2 ? idv.z : idv.w;
-    const int phk = __builtin_amdgcn_readfirstlane(ik);
-    const int phv = __builtin_amdgcn_readfirstlane(iv);
-    const size_t slk = (size_t)((unsigned)phk < (unsigned)p.num_pages ? phk : 0) * p.hkv + kvh;
-    const size_t slv = (size_t)((unsigned)phv < (unsigned)p.num_pages ? phv : 0) * p.hkv + kvh;
-    const uint8_t* kb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.k_cache + slk * 16 * D));
-    const uint8_t* vb = reinterpret_cast<const uint8_t*>(uniform_ptr(p.v_cache + slv * D * 16));
-    // the chunk's byte offset in both slabs: K row rem / (D/8), 8-dim chunk rem % (D/8);
-    // V row rem / 2, 8-token half rem % 2.  Both are 16 rem bytes.  An unsigned
-    // 32-bit offset from a uniform base lets the load take its scalar-base form.
-    uint32_t off = 16u * (uint32_t)rem;
-    asm volatile("" : "+v"(off));  // keeps the offset 32-bit at the load (not hoisted as a 64-bit value)
-    st.k[i] = kv_load<CB_NT_PREFILL>(reinterpret_cast<const uint4*>(kb + off));
-    st.v[i] = kv_load<CB_NT_PREFILL>(reinterpret_cast<const uint4*>(vb + off));
+  for (int j = 0; j < PfDmaOffsets<D>::NJ; ++j) o[j] = od.k[j];
+  o[PfDmaOffsets<D>::NJ] = od.v;
+#pragma unroll
+  for (int j = 0; j <= PfDmaOffsets<D>::NJ; ++j) asm volatile("" : "+v"(o[j]));
+  lds_copy16<0>(kb + o[0], kl);
+  lds_copy16<1>(kb + o[1], kl);
+  if constexpr (PfDmaOffsets<D>::NJ > 2) {
+    lds_copy16<2>(kb + o[2], kl);
+    lds_copy16<3>(kb + o[3], kl);
+  }
+  const uint32_t ov = o[PfDmaOffsets<D>::NJ];
+  lds_copy16<0>(vb + ov, vl);
+  lds_copy16<1>(vb + ov, vl);
+  if constexpr (PfDmaOffsets<D>::NJ > 2) {
+    lds_copy16<2>(vb + ov, vl);
+    lds_copy16<3>(vb + ov, vl);
   }
 }
 
-// Stage the registers' K half at kl and their V half (tile ktv) at vl.  V
-// tokens at or past the context end, and below the row tile's first key
-// (`kfloor`: pages there may have been released), are zeroed here, where the
-// loaded data is consumed anyway.
-template <int D, bool WIN>
-__device__ __forceinline__ void pf_store(const PfStage<D>& st, uint8_t* kl, uint8_t* vl, int ktv, int ctx,
-                                         int kfloor, int tid) {
-  using Lds = PfLds<D>;
-  // uniform: only the tile that holds the context end (or the window floor) masks
-  const bool tail = (ktv + 1) * PF_KEYS > ctx;
-  const bool below = WIN && ktv * PF_KEYS < kfloor;
+// Wait for this wave's LDS copies (vmcnt 0; the other counters untouched).
+__device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Order of the N LDS fragment reads and the N MFMAs that take them, one each
+// (scheduler groups), in batches of R: the next batch's reads go out right
+// after the first MFMA of the current one.  While LDS copies are in flight
+// the compiler waits for all outstanding LDS reads before an MFMA that needs
+// one; in this order such a wait only covers reads issued R-1 MFMAs earlier.
+template <int N>
+__device__ __forceinline__ void pf_read_schedule() {
+  constexpr int R = CB_PF_READAHEAD;
+  static_assert(R > 0 && N % R == 0, "batches of R");
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // DS reads
 #pragma unroll
-  for (int i = 0; i < PfStage<D>::N; ++i) {
-    const int e = tid + PF_THREADS * i;
-    const int pgl = e / (2 * D), rem = e % (2 * D);
-    const int r = rem / (D / 8), c16 = rem % (D / 8);
-    *reinterpret_cast<uint4*>(kl + (pgl * 16 + r) * Lds::KROW + c16 * 16) = st.k[i];
-    const int dr = rem >> 1, hf = rem & 1;
-    // tokens 8hf..8hf+7 of row dr, the halves of rows with bit 3 set swapped
-    // (rows r and r + 8 are 256 bytes apart: same banks for the same half)
-    uint8_t* dst = vl + (pgl * D + dr) * Lds::VROW + 16 * (hf ^ ((dr >> 3) & 1));
-    uint4 vv = st.v[i];
-    const int k8 = (ktv * 4 + pgl) * 16 + hf * 8;  // key of the first of these 8 tokens
-    const int n = ctx - k8;                          // valid tokens among these 8
-    if (tail && n < 8) {
-      vv.x = keep16(vv.x, 0, n);
-      vv.y = keep16(vv.y, 2, n);
-      vv.z = keep16(vv.z, 4, n);
-      vv.w = keep16(vv.w, 6, n);
-    }
-    const int nlo = kfloor - k8;                     // tokens below the first key
-    if (below && nlo > 0) {
-      vv.x = drop16(vv.x, 0, nlo);
-      vv.y = drop16(vv.y, 2, nlo);
-      vv.z = drop16(vv.z, 4, nlo);
-      vv.w = drop16(vv.w, 6, nlo);
-    }
-    *reinterpret_cast<uint4*>(dst) = vv;
+  for (int b = 0; b < N / R; ++b) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (b + 1 < N / R) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, R - 1, 0);
   }
 }
 
 template <int D, bool WIN>
-__device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* smem) {
+__device__ __forceinline__ void prefill_tile(const Params& p, int b) {
   using Lds = PfLds<D>;
   const int kvh = b % p.hkv;
   const int j = b / p.hkv;
@@ -733,19 +750,23 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   constexpr int NO = D / 32;  // 32-dim output tiles
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
   // the item's page ids, staged once (at most PF_MAX_PAGES; the host caps the key range)
-  int* pids = reinterpret_cast<int*>(smem + Lds::BYTES);
+  // separate arrays per stage: the compiler can then tell that a copy in
+  // flight into one stage does not touch the stage being read
+  // (the stages, larger and more aligned, are laid out first: the copies'
+  // LDS destinations stay below 64 KB)
+  static_assert(PF_WAVES == 4, "one wave per page of a 64-key tile");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_st0[Lds::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_st1[Lds::STAGE];
+  __shared__ __attribute__((aligned(4))) int lds_ids[PF_MAX_PAGES];
+  int* pids = lds_ids;
   for (int i = tid; i < (kt1 - kt0) * 4; i += PF_THREADS) {
     const int pg = kt0 * 4 + i;
     pids[i] = pg < npages ? btrow[pg] : -1;
   }
   __syncthreads();
-  // three-stage pipeline: tile kt+2 loads into registers while tile kt+1 sits
-  // in the second LDS stage and tile kt is computed.  Fetches past the last
-  // tile re-read it (clamped), so every iteration issues the same loads and
-  // the compiler never has to drain the one still in flight.
-  // The query fragments first: they are waited for once, here, while the
-  // first two K/V tiles stay in flight (a load still pending at the loop
-  // header would make the compiler wait inside the loop, draining the pipeline).
+  // The query fragments first: they are waited for once, before the loop (a
+  // load still pending at the loop header would make the compiler wait for
+  // it inside the loop, behind the tile copies).
   bf16x8 qf[NK];
   {
     const uint16_t* qrow = p.q + ((size_t)(t0 + qi) * p.hq + kvh * G + hh) * D + 8 * gg;
@@ -753,12 +774,16 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
     for (int cc = 0; cc < NK; ++cc)
       qf[cc] = as_bf16x8(rvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * cc) : make_uint4(0, 0, 0, 0));
   }
-  PfStage<D> sa, sb;
-  const int klast = kt1 - 1;
-  if (kt0 < kt1) {
-    pf_fetch<D>(sa, p, pids, kt0, kt0, kt0, kvh, tid);
-    pf_fetch<D>(sb, p, pids, min(kt0 + 1, klast), min(kt0 + 1, klast), kt0, kvh, tid);
-  }
+  // the first tile's copy starts now; the loop below keeps one tile in flight
+  const int wu = __builtin_amdgcn_readfirstlane(wv);
+  const PfDmaOffsets<D> od(lane);
+  uint8_t* stage0 = lds_st0;
+  uint8_t* stage1 = lds_st1;
+  if (kt0 < kt1) pf_dma<D>(stage0, p, pids, kt0, kt0, kvh, wu, od);
+  // this lane's K read offsets in a stage: row krow, logical chunk 2 cc + gg
+  uint32_t krd[NK];
+#pragma unroll
+  for (int cc = 0; cc < NK; ++cc) krd[cc] = (uint32_t)(krow * Lds::KROW + 16 * ((2 * cc + gg) ^ kswz<D>(krow)));
 #pragma unroll
   for (int cc = 0; cc < NK; ++cc) {
     const uint4 qq = __builtin_bit_cast(uint4, qf[cc]);
@@ -772,9 +797,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
   float m = -INFINITY, l = 0.f;
   const float c = p.scale_log2;
 
-  uint8_t* stage0 = smem;
-  uint8_t* stage1 = smem + Lds::STAGE;
-  if (kt0 < kt1) pf_store<D, WIN>(sa, stage0, stage0 + Lds::K_BYTES, kt0, ctx, kfloor, tid);
+  wait_lds_copies();
   __syncthreads();
   auto tile_step = [&](int kt, const uint8_t* cur) {
     const int kbase = kt * PF_KEYS;
@@ -787,16 +810,20 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       // keys the P V product takes from it, with no exchange between lanes.
       floatx16 sc[2];
       if (CB_PF_PRIO) __builtin_amdgcn_s_setprio(1);  // the other wave's VALU work fills the MFMA gaps
+      // the two subtiles' accumulations alternate; the K fragment reads go
+      // out in batches ahead of their MFMAs
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[sub][r] = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NK; ++cc) {
-          const uint4 ka = *reinterpret_cast<const uint4*>(kl + (sub * 32 + krow) * Lds::KROW + (16 * cc + 8 * gg) * 2);
+      for (int cc = 0; cc < NK; ++cc)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(kl + sub * 32 * Lds::KROW + krd[cc]);
           sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qf[cc], sc[sub], 0, 0, 0);
         }
-      }
+      if constexpr (CB_PF_READAHEAD > 0) pf_read_schedule<2 * NK>();
       if (CB_PF_PRIO) __builtin_amdgcn_s_setprio(0);
       // straddles this wave's diagonal (or the context end), or its window's lower edge
       if (kbase + PF_KEYS > w_kfull || (WIN && kbase < w_klo_max)) {
@@ -834,36 +861,62 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
       // taken from the same bf16 P (a two-term dot product with ones per
       // packed pair), so the normaliser weighs exactly what P V does.
       float rsum[2] = {0.f, 0.f};
+      // MASKV: V tokens at or past the context end, or below the tile's
+      // first key, are zeroed as they are read (the copy brings whatever the
+      // page holds there; P is 0 for them, but 0 * NaN is not)
+      auto pv = [&](auto maskv) {
+        constexpr bool MASKV = decltype(maskv)::value;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int r0 = 8 * half;
-          const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
-                                      pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
-                                      pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
-                                      pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
-          rsum[half] = sum_bf16x8(pb, rsum[half]);
-          const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
+          for (int half = 0; half < 2; ++half) {
+            const int r0 = 8 * half;
+            const uint4 pb = make_uint4(pack_bf16x2(sc[sub][r0 + 0], sc[sub][r0 + 1]),
+                                        pack_bf16x2(sc[sub][r0 + 2], sc[sub][r0 + 3]),
+                                        pack_bf16x2(sc[sub][r0 + 4], sc[sub][r0 + 5]),
+                                        pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
+            rsum[half] = sum_bf16x8(pb, rsum[half]);
+            const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
+            const int k8 = kbase + (2 * sub + half) * 16 + 8 * gg;  // key of this lane's first V token
 #pragma unroll
-          for (int dt = 0; dt < NO; ++dt) {
-            const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + vhalf);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
+            for (int dt = 0; dt < NO; ++dt) {
+              uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + vhalf);
+              if constexpr (MASKV) {
+                const int n = ctx - k8;
+                va.x = keep16(va.x, 0, n);
+                va.y = keep16(va.y, 2, n);
+                va.z = keep16(va.z, 4, n);
+                va.w = keep16(va.w, 6, n);
+                if (WIN) {
+                  const int nlo = kfloor - k8;
+                  va.x = drop16(va.x, 0, nlo);
+                  va.y = drop16(va.y, 2, nlo);
+                  va.z = drop16(va.z, 4, nlo);
+                  va.w = drop16(va.w, 6, nlo);
+                }
+              }
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
+            }
           }
-        }
+        if constexpr (CB_PF_READAHEAD > 0) pf_read_schedule<4 * NO>();  // V fragments likewise
+      };
+      if (kbase + PF_KEYS > ctx || (WIN && kbase < kfloor)) pv(std::true_type{});
+      else pv(std::false_type{});
       l += rsum[0] + rsum[1];
     }
   };
+  // two LDS stages: tile kt+1 is copied into one while tile kt is computed
+  // from the other; the barrier after each tile both publishes the next
+  // tile's copy and frees the stage just read
   for (int kt = kt0; kt < kt1; kt += 2) {
-    const int k2 = min(kt + 2, klast), k1 = min(kt + 1, klast), k3 = min(kt + 3, klast);
-    pf_fetch<D>(sa, p, pids, k2, k2, kt0, kvh, tid);
+    if (kt + 1 < kt1) pf_dma<D>(stage1, p, pids, kt + 1, kt0, kvh, wu, od);
     tile_step(kt, stage0);
-    pf_store<D, WIN>(sb, stage1, stage1 + Lds::K_BYTES, k1, ctx, kfloor, tid);  // tile kt+1 (clamped)
+    wait_lds_copies();
     __syncthreads();
     if (kt + 1 >= kt1) break;
-    pf_fetch<D>(sb, p, pids, k3, k3, kt0, kvh, tid);
+    if (kt + 2 < kt1) pf_dma<D>(stage0, p, pids, kt + 2, kt0, kvh, wu, od);
     tile_step(kt + 1, stage1);
-    pf_store<D, WIN>(sa, stage0, stage0 + Lds::K_BYTES, k2, ctx, kfloor, tid);  // tile kt+2 (clamped)
+    wait_lds_copies();
     __syncthreads();
   }
 
@@ -900,7 +953,6 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b, uint8_t* sm
 // ---------------------------------------------------------------------------
 template <int D, bool WIN>
 __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[PfLds<D>::TOTAL];
   const int b = blockIdx.x;
   const int np = p.pf_blocks, nd = p.dec_blocks;
   // live blocks first, in the order the header names; a grid sized by the
@@ -926,7 +978,7 @@ __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kerne
     return;  // past the live work (the grid is sized by the caps): nothing to do
   }
   if (pf >= 0) {
-    prefill_tile<D, WIN>(p, pf, smem);
+    prefill_tile<D, WIN>(p, pf);
     return;
   }
   decode_wave<D, WIN, false>(p, dec * PF_WAVES + (threadIdx.x >> 6));
