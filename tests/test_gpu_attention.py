@@ -190,9 +190,12 @@ def test_chunk_size_invariance_bf16():
         compare(np.concatenate(outs), ref, "bf16", f"chunk {chunk}", am)
 
 
-def test_nan_in_unused_slots_does_not_leak():
-    """Garbage (NaN) in partial-page tails and in unreferenced pages is masked."""
-    st = Step([(17, 1), (33, 1), (4097, 1), (45, 13), (129, 129)], 16, 4, 128, "bf16", seed=8,
+@pytest.mark.parametrize("d", [64, 128])
+def test_nan_in_unused_slots_does_not_leak(d):
+    """Garbage (NaN) in partial-page tails and in unreferenced pages is masked
+    (prefill: the V tokens of the tile that holds the context end are zeroed
+    as they are read from LDS)."""
+    st = Step([(17, 1), (33, 1), (4097, 1), (45, 13), (129, 129), (300, 77)], 16, 4, d, "bf16", seed=8,
               fill=float("nan"))
     kc, vc = st.upload()
     out = st.run(kc, vc)
