@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--workload", default="mixed", choices=["mixed", "decode", "long", "chunk", "trace"],
                     help="trace: the 256-request FIFO trace run once, every step timed cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-csv", default="", help="trace workload: also write one CSV row per step here")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
     ap.add_argument("--page-order", default="shuffled", choices=["shuffled", "sequential"],
                     help="physical page ids: a seeded random permutation (default) or handed out in order")
@@ -306,7 +307,7 @@ def run_trace(args, dev):
     for e in ev:
         e.record()
     pending, step = list(reqs), 0
-    rows = []                          # (tokens, bytes, flops, span_s, kernel_s, class)
+    rows = []                          # (tokens, bytes, flops, span_s, kernel_s, class, seqs, decodes, max ctx)
     frag = []
     t0 = time.perf_counter()
     while True:
@@ -334,11 +335,17 @@ def run_trace(args, dev):
         torch.cuda.synchronize()
         nbytes, flops, _ = algorithmic(desc, hq, hkv, d, esize)
         cls = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
-        rows.append((T, nbytes, flops, ev[0].elapsed_time(ev[1]) / 1e3, ev[2].elapsed_time(ev[3]) / 1e3, cls))
+        rows.append((T, nbytes, flops, ev[0].elapsed_time(ev[1]) / 1e3, ev[2].elapsed_time(ev[3]) / 1e3, cls,
+                     desc.num_seqs, desc.num_decodes, int(desc.context_lens.max())))
         st = layer.builder.stats()
         if st["allocated_slots"]:
             frag.append(st["fragmentation"])
     wall = time.perf_counter() - t0
+    if args.trace_csv:
+        with open(args.trace_csv, "w") as f:
+            f.write("query_tokens,alg_bytes,alg_flops,span_s,kernel_s,class,seqs,decodes,max_ctx\n")
+            for r in rows:
+                f.write(",".join(str(x) for x in r) + "\n")
     tok = sum(r[0] for r in rows)
     span = sum(r[3] for r in rows)
     classes = {}
