@@ -749,15 +749,15 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
   constexpr int NK = D / 16;  // QK k-steps of 16 dims
   constexpr int NO = D / 32;  // 32-dim output tiles
   const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
-  // the item's page ids, staged once (at most PF_MAX_PAGES; the host caps the key range)
-  // separate arrays per stage: the compiler can then tell that a copy in
-  // flight into one stage does not touch the stage being read
-  // (the stages, larger and more aligned, are laid out first: the copies'
-  // LDS destinations stay below 64 KB)
+  // LDS: two tile stages and the item's page ids.  The stages are separate
+  // arrays so that the compiler can tell a copy in flight into one stage does
+  // not touch the stage being read; being larger and more aligned they are
+  // laid out first, which keeps the copies' LDS destinations below 64 KB.
   static_assert(PF_WAVES == 4, "one wave per page of a 64-key tile");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_st0[Lds::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_st1[Lds::STAGE];
   __shared__ __attribute__((aligned(4))) int lds_ids[PF_MAX_PAGES];
+  // the item's page ids, staged once (at most PF_MAX_PAGES; the host caps the key range)
   int* pids = lds_ids;
   for (int i = tid; i < (kt1 - kt0) * 4; i += PF_THREADS) {
     const int pg = kt0 * 4 + i;
