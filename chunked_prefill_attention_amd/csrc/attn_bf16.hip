@@ -81,6 +81,9 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_DEC_MIN_WAVES     // decode splits: the longest that still gives this many wavefronts
 #define CB_DEC_MIN_WAVES 8192
 #endif
+#ifndef CB_DEC_MIN_WAVES_ALONE  // ... in a step without prefill work (the decode-only launch)
+#define CB_DEC_MIN_WAVES_ALONE 4096
+#endif
 #ifndef CB_PF_PRIO          // wave priority raised while the prefill QK MFMAs issue
 #define CB_PF_PRIO 1
 #endif
@@ -1215,12 +1218,14 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t max_pages = (max_context_len + 15) / 16;
   const int64_t G = hkv > 0 ? hq / hkv : 1;
   // decode: the longest split (pages per wavefront) that still gives the
-  // decode grid >= 8k wavefronts (about 2-3 rounds of the chip's wave slots);
-  // longer splits write fewer partials for the combine
+  // decode grid >= 8k wavefronts (about 2-3 rounds of the chip's wave slots),
+  // or >= 4k when no prefill work shares the launch; longer splits write
+  // fewer partials for the combine and start fewer wavefronts
   const int64_t lanes = (int64_t)num_decodes * hkv;
+  const int64_t min_waves = num_seqs > num_decodes ? CB_DEC_MIN_WAVES : CB_DEC_MIN_WAVES_ALONE;
   pl.split_pages = 8;
   for (int sp : {64, 32, 16}) {
-    if (lanes * ((max_pages + sp - 1) / sp) >= CB_DEC_MIN_WAVES) { pl.split_pages = sp; break; }
+    if (lanes * ((max_pages + sp - 1) / sp) >= min_waves) { pl.split_pages = sp; break; }
   }
   pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);
   // prefill: row tiles bound by the query tokens; key ranges cut so that about
