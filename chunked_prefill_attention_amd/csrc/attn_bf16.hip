@@ -115,6 +115,7 @@ constexpr int PF_THREADS = CB_PF_THREADS;   // threads of a prefill workgroup
 constexpr int PF_WAVES = PF_THREADS / 64;
 constexpr int PF_ROWS = PF_WAVES * 32;      // query rows per prefill workgroup (32 per wave)
 constexpr int PF_KEYS = 64;   // keys per prefill tile (4 pages)
+constexpr int DEC_MAX_SPLIT = 128;                         // pages one decode item covers at most
 constexpr int PF_MAX_PAGES = 512;                          // page ids one prefill item stages in LDS
 constexpr int PF_MAX_KEYS = (PF_MAX_PAGES - 4) * 16 / PF_KEYS * PF_KEYS;  // largest key range per item
 constexpr float LOG2E = 1.4426950408889634f;
@@ -331,9 +332,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   // decode items, longest first: every full split (split_pages pages) of every
   // sequence, then each sequence's shorter last split, by decreasing length.
   // dec_first[s] = first full split of s; dec_rem[s] = its short split or -1.
-  __shared__ int bucket[65], cursor[65];
-  const int SP = p.split_pages;  // <= 64
-  if (tid <= 64) { bucket[tid] = 0; cursor[tid] = 0; }
+  __shared__ int bucket[DEC_MAX_SPLIT + 1], cursor[DEC_MAX_SPLIT + 1];
+  const int SP = p.split_pages;  // <= DEC_MAX_SPLIT
+  if (tid <= DEC_MAX_SPLIT) { bucket[tid] = 0; cursor[tid] = 0; }
   __syncthreads();
   int carry = 0;
   for (int base = 0; base < p.num_decodes; base += 1024) {
@@ -354,9 +355,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
     carry += total;
   }
   __syncthreads();
-  if (tid < 64) {  // bucket starts: one wave scans the 64 bucket counts
-    const int n = bucket[tid];
-    bucket[tid] = carry + wave_inclusive_scan(n) - n;
+  {  // bucket starts: an exclusive scan of the bucket counts
+    const int n = tid < DEC_MAX_SPLIT ? bucket[tid] : 0;
+    int total;
+    const int ex = block_exclusive_scan(n, sh, total);
+    if (tid < DEC_MAX_SPLIT) bucket[tid] = carry + ex;
   }
   __syncthreads();
   for (int base = 0; base < p.num_decodes; base += 1024) {
@@ -371,11 +374,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
         if (idx < p.dec_cap) p.dec_items[idx] = make_int4(s, nfull, ctx, p.qsl[s]);
       }
       p.dec_rem[s] = idx;
-      if (rem > 0) atomicMax(&cursor[64], idx + 1);
+      if (rem > 0) atomicMax(&cursor[DEC_MAX_SPLIT], idx + 1);
     }
   }
   __syncthreads();
-  const int dec_total = max(carry, cursor[64]);
+  const int dec_total = max(carry, cursor[DEC_MAX_SPLIT]);
   for (int i = dec_total + tid; i < p.dec_cap; i += 1024) p.dec_items[i] = make_int4(-1, 0, 0, 0);
 
   // prefill tiles and their key splits; heaviest (last) tiles first
@@ -545,9 +548,12 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int koff = hl * D + g * 8;
   const int voff = hl * 16 + g * 4;
 
-  // this split's physical page ids, one per lane (split_pages <= 64); the wait
+  // this split's physical page ids, one per lane in two registers (pages
+  // 0..63 and 64..127 of the split, split_pages <= DEC_MAX_SPLIT); the wait
   // for them happens here, before any page load is in flight
+  static_assert(DEC_MAX_SPLIT <= 128, "two page ids per lane");
   const int my_page = __builtin_amdgcn_readfirstlane(0) + ((lane < pg1 - pg0) ? btrow[pg0 + lane] : 0);
+  const int my_page2 = pg1 - pg0 > 64 ? ((lane + 64 < pg1 - pg0) ? btrow[pg0 + 64 + lane] : 0) : 0;
   const int first_page = __builtin_amdgcn_readlane(my_page, 0);
   // ring of NB page buffers: page pg+PF is loading while page pg is computed
   constexpr int PF = CB_DEC_PREFETCH;
@@ -576,8 +582,11 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
     for (int r = 0; r < NB; ++r) {
       const int cur = pg + r;
       const int nxt = cur + PF;
-      // readlane's lane index wraps past 63; the page is then unused (nxt >= pg1)
-      const int phys = nxt < pg1 ? __builtin_amdgcn_readlane(my_page, (nxt - pg0) & 63) : -1;
+      // the lane index is taken mod 64 (pages past pg1 are never used)
+      const int ix = nxt - pg0;
+      const int phys = nxt < pg1 ? (ix < 64 ? __builtin_amdgcn_readlane(my_page, ix & 63)
+                                            : __builtin_amdgcn_readlane(my_page2, ix & 63))
+                                 : -1;
       decode_issue<D, NT>(buf[(r + PF) % NB], p, phys, kvh, koff, voff);
       if (cur < pg1) decode_compute<D, WIN>(buf[r], cur, ctx, lo, g, qf, o, m, l, c);
     }
@@ -1224,7 +1233,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t lanes = (int64_t)num_decodes * hkv;
   const int64_t min_waves = num_seqs > num_decodes ? CB_DEC_MIN_WAVES : CB_DEC_MIN_WAVES_ALONE;
   pl.split_pages = 8;
-  for (int sp : {64, 32, 16}) {
+  for (int sp : {DEC_MAX_SPLIT, 64, 32, 16}) {
     if (lanes * ((max_pages + sp - 1) / sp) >= min_waves) { pl.split_pages = sp; break; }
   }
   pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);
@@ -1294,7 +1303,7 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
   int32_t* rem_at = reinterpret_cast<int32_t*>(base + L.dec_rem);
   const int SP = pl.split_pages;
   int64_t n = 0;
-  int counts[65] = {0};
+  int counts[DEC_MAX_SPLIT + 1] = {0};
   for (int s = 0; s < num_decodes; ++s) {
     const int np = decode_pages(ctx[s], window);
     const int nfull = np / SP, rem = np - nfull * SP;
@@ -1302,8 +1311,8 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
     for (int k = 0; k < nfull && n < pl.dec_cap; ++k) dec[n++] = make_int4(s, k, ctx[s], qsl[s]);
     if (rem > 0) counts[SP - rem]++;
   }
-  int starts[65];
-  for (int b = 0, acc = (int)n; b <= 64; ++b) { starts[b] = acc; acc += counts[b]; }
+  int starts[DEC_MAX_SPLIT + 1];
+  for (int b = 0, acc = (int)n; b <= DEC_MAX_SPLIT; ++b) { starts[b] = acc; acc += counts[b]; }
   for (int s = 0; s < num_decodes; ++s) {
     const int np = decode_pages(ctx[s], window);
     const int nfull = np / SP, rem = np - nfull * SP;

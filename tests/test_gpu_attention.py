@@ -203,6 +203,22 @@ def test_nan_in_unused_slots_does_not_leak(d):
     _check_all(st, out, "nan tails")
 
 
+@pytest.mark.parametrize("with_prefill", [False, True])
+def test_long_decode_splits_match_oracle(with_prefill):
+    """256 decode sequences, two of them long (1,025 and 1,000 pages): with
+    2,048 (sequence, KV head) lanes the planner picks 128-page decode splits,
+    in the decode-only launch and beside a prefill chunk, so the long
+    sequences run as full 128-page splits plus a short last one (1 and 104
+    pages), listed by the device plan kernel of a direct call."""
+    seqs = [(16400, 1), (16000, 1)] + [(17 + 13 * i, 1) for i in range(254)]
+    if with_prefill:
+        seqs.append((300, 77))
+    st = Step(seqs, 32, 8, 128, "bf16", seed=21)
+    kc, vc = st.upload()
+    out = st.run(kc, vc)
+    _check_all(st, out, "long decode splits")
+
+
 def test_bad_page_ids_do_not_fault():
     """Out-of-range block-table entries (a broken precondition) must not fault:
     they read page 0, so with finite cache contents the output stays finite."""
