@@ -1229,11 +1229,16 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   // decode: the longest split (pages per wavefront) that still gives the
   // decode grid >= 8k wavefronts (about 2-3 rounds of the chip's wave slots),
   // or >= 4k when no prefill work shares the launch; longer splits write
-  // fewer partials for the combine and start fewer wavefronts
+  // fewer partials for the combine and start fewer wavefronts.  max_pages is
+  // the step's longest context, which in a mixed step is usually a prefill
+  // sequence's, so there the wave count is overestimated: mixed launches
+  // stop at 64-page splits.
   const int64_t lanes = (int64_t)num_decodes * hkv;
-  const int64_t min_waves = num_seqs > num_decodes ? CB_DEC_MIN_WAVES : CB_DEC_MIN_WAVES_ALONE;
+  const bool with_prefill = num_seqs > num_decodes;
+  const int64_t min_waves = with_prefill ? CB_DEC_MIN_WAVES : CB_DEC_MIN_WAVES_ALONE;
   pl.split_pages = 8;
   for (int sp : {DEC_MAX_SPLIT, 64, 32, 16}) {
+    if (with_prefill && sp > 64) continue;
     if (lanes * ((max_pages + sp - 1) / sp) >= min_waves) { pl.split_pages = sp; break; }
   }
   pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);

@@ -206,9 +206,9 @@ def test_nan_in_unused_slots_does_not_leak(d):
 @pytest.mark.parametrize("with_prefill", [False, True])
 def test_long_decode_splits_match_oracle(with_prefill):
     """256 decode sequences, two of them long (1,025 and 1,000 pages): with
-    2,048 (sequence, KV head) lanes the planner picks 128-page decode splits,
-    in the decode-only launch and beside a prefill chunk, so the long
-    sequences run as full 128-page splits plus a short last one (1 and 104
+    2,048 (sequence, KV head) lanes the planner picks 128-page decode splits
+    in the decode-only launch (full splits plus a short last one of 1 and 104
+    pages) and 64-page splits beside a prefill chunk (last ones of 1 and 40
     pages), listed by the device plan kernel of a direct call."""
     seqs = [(16400, 1), (16000, 1)] + [(17 + 13 * i, 1) for i in range(254)]
     if with_prefill:
