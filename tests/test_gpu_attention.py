@@ -219,6 +219,21 @@ def test_long_decode_splits_match_oracle(with_prefill):
     _check_all(st, out, "long decode splits")
 
 
+@pytest.mark.parametrize("d,window", [(64, 0), (128, 9000), (64, 2500)])
+def test_long_decode_splits_d64_and_window(d, window):
+    """128-page decode splits at D 64 and under a sliding window (a split's
+    pages then start at the window's first page, and the second page-id
+    register holds pages 64..127 of the split)."""
+    seqs = [(16400, 1), (16000, 1)] + [(17 + 13 * i, 1) for i in range(254)]
+    st = Step(seqs, 16, 8, d, "bf16", seed=22 + d + window)
+    kc, vc = st.upload()
+    q = to_dev(np.concatenate(st.q), "bf16")
+    out = cb.attention_step(q, kc, vc, i32(st.bt), i32(st.qsl), i32(st.ctx), i32(st.off), st.num_decodes,
+                            st.max_ctx, st.scale, sliding_window=window)
+    torch.cuda.synchronize()
+    _check_all(st, out, f"long splits d{d} w{window}", window=window)
+
+
 def test_bad_page_ids_do_not_fault():
     """Out-of-range block-table entries (a broken precondition) must not fault:
     they read page 0, so with finite cache contents the output stays finite."""
