@@ -90,6 +90,12 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #ifndef CB_NT_DECODE        // decode-only launch: K/V page loads with the non-temporal hint
 #define CB_NT_DECODE 1
 #endif
+#ifndef CB_NT_MIXED         // the same for the decode waves of the mixed launch ...
+#define CB_NT_MIXED 0
+#endif
+#ifndef CB_NT_MIXED_WINDOW  // ... and of its sliding-window instantiation
+#define CB_NT_MIXED_WINDOW 1
+#endif
 #ifndef CB_PF_READAHEAD     // prefill: K and V fragments read from LDS in batches of this many (0: compiler's order)
 #define CB_PF_READAHEAD 4
 #endif
@@ -520,8 +526,9 @@ __device__ __forceinline__ void decode_compute(DecodeBuf<D>& B, int pg, int ctx,
     o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(B.v[t]), as_short4(pk), o[t], 0, 0, 0);
 }
 
-// NT: page loads with the non-temporal hint (the decode-only launch; in the
-// mixed launch plain loads measured slightly faster)
+// NT: page loads with the non-temporal hint (the decode-only launch and the
+// windowed mixed launch; in the unwindowed mixed launch plain loads measured
+// slightly faster)
 template <int D, bool WIN, bool NT>
 __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int kvh = w % p.hkv;
@@ -993,7 +1000,7 @@ __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kerne
     prefill_tile<D, WIN>(p, pf);
     return;
   }
-  decode_wave<D, WIN, false>(p, dec * PF_WAVES + (threadIdx.x >> 6));
+  decode_wave<D, WIN, (WIN ? CB_NT_MIXED_WINDOW : CB_NT_MIXED) != 0>(p, dec * PF_WAVES + (threadIdx.x >> 6));
 }
 
 template <int D, bool WIN>
@@ -1222,7 +1229,7 @@ int mixed_slots(int head_dim) {
 }
 
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq, int32_t hkv,
-                   int32_t head_dim, int32_t max_context_len) {
+                   int32_t head_dim, int32_t max_context_len, int32_t window) {
   Bf16Plan pl{};
   const int64_t max_pages = (max_context_len + 15) / 16;
   const int64_t G = hkv > 0 ? hq / hkv : 1;
@@ -1241,7 +1248,25 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
     if (with_prefill && sp > 64) continue;
     if (lanes * ((max_pages + sp - 1) / sp) >= min_waves) { pl.split_pages = sp; break; }
   }
-  pl.dec_cap = (int64_t)num_decodes * ((max_pages + pl.split_pages - 1) / pl.split_pages);
+  // the items per decode sequence this allows sizes the work lists and the
+  // partials (the workspace bound, which does not depend on the window)
+  const int64_t budget = (max_pages + pl.split_pages - 1) / pl.split_pages;
+  pl.dec_cap = (int64_t)num_decodes * budget;
+  if (window > 0) {
+    // a decode reads only its window's pages: within the same item budget,
+    // the longest split that still reaches the wavefront count, else the
+    // one that gives the most wavefronts
+    const int64_t wpages = std::min<int64_t>(max_pages, ((int64_t)window + 15) / 16 + 1);
+    int best = pl.split_pages;
+    for (int sp : {DEC_MAX_SPLIT, 64, 32, 16, 8}) {
+      if (with_prefill && sp > 64) continue;
+      const int64_t items = (wpages + sp - 1) / sp;
+      if (items > budget) break;  // shorter splits need even more items
+      best = sp;
+      if (lanes * items >= min_waves) break;
+    }
+    pl.split_pages = best;
+  }
   // prefill: row tiles bound by the query tokens; key ranges cut so that about
   // 1024 workgroups exist when the tiles are long, never below 512 keys
   const int64_t np = num_seqs - num_decodes;

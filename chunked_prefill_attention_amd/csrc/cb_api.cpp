@@ -189,7 +189,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
     return device_status(cb::launch_attention_f32(a, st), "cb_attention_step launch (f32)");
   }
   const cb::Bf16Plan plan = cb::plan_bf16(num_seqs, num_decodes, num_tokens, num_q_heads, num_kv_heads,
-                                          head_dim, max_context_len);
+                                          head_dim, max_context_len, sliding_window);
   if (plan.dec_cap * num_kv_heads >= (int64_t(1) << 31) || plan.pf_item_cap * num_kv_heads >= (int64_t(1) << 30) ||
       plan.pf_tile_cap * num_kv_heads >= (int64_t(1) << 27))   // the prefill combine runs 8 blocks per tile
     return cb::fail(CB_ERR_INVALID, "step too large for one launch");

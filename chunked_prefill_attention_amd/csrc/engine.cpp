@@ -231,7 +231,8 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   if (e->cfg.dtype == CB_BF16 && e->x_ntok > 0) {
     // the attention step's work lists, built here instead of by a device plan kernel
     cb::Bf16Plan pl = cb::plan_bf16(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads,
-                                    e->cfg.num_kv_heads, e->cfg.head_dim, std::max(e->x_maxctx, 1));
+                                    e->cfg.num_kv_heads, e->cfg.head_dim, std::max(e->x_maxctx, 1),
+                                    e->cfg.builder.sliding_window);
     pl.slots = cb::mixed_slots(e->cfg.head_dim);  // the lists' block order depends on it
     const cb::WorkListLayout lay = cb::work_list_layout(pl, e->x_ndec);
     const size_t at = (off + 3) & ~size_t(3);  // 16-byte aligned (int32 units)

@@ -59,7 +59,7 @@ struct Bf16Plan {
 // occupancy per CU times the CU count; queried once per device and head size).
 int mixed_slots(int head_dim);
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
-                   int32_t hkv, int32_t head_dim, int32_t max_context_len);
+                   int32_t hkv, int32_t head_dim, int32_t max_context_len, int32_t window = 0);
 
 // Work lists of one bf16 step built by the caller (the engine builds them on
 // the host and uploads them with the step's metadata); when given, the
