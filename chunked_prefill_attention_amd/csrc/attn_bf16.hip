@@ -387,47 +387,72 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   const int dec_total = max(carry, cursor[DEC_MAX_SPLIT]);
   for (int i = dec_total + tid; i < p.dec_cap; i += 1024) p.dec_items[i] = make_int4(-1, 0, 0, 0);
 
-  // prefill tiles and their key splits; heaviest (last) tiles first
+  // prefill tiles and their key splits; heaviest (last) tiles first.  One
+  // wavefront lists one sequence (its lanes share the row tiles), 16 at a
+  // time; a block-wide scan over the sequences places them.
+  __shared__ int seq_tiles[1024], seq_items[1024], seq_tex[1024], seq_iex[1024];
+  const int lane = tid & 63, wv = tid >> 6;
   int tcarry = 0, icarry = 0;
   for (int base = p.num_decodes; base < p.num_seqs; base += 1024) {
-    const int s = base + tid;
-    int ntiles = 0, nitems = 0, L = 0, ctx = 0, off = 0;
-    if (s < p.num_seqs) {
-      L = p.qsl[s + 1] - p.qsl[s];
-      ctx = p.ctx_lens[s];
-      off = p.q_off[s];
-      ntiles = L > 0 ? (L * p.G + PF_ROWS - 1) / PF_ROWS : 0;
-      for (int t = 0; t < ntiles; ++t) nitems += tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
+    const int nchunk = min(1024, p.num_seqs - base);
+    // counts: tiles and items (key splits) of each sequence
+    for (int i = wv; i < nchunk; i += 16) {
+      const int s = base + i;
+      const int L = p.qsl[s + 1] - p.qsl[s], ctx = p.ctx_lens[s], off = p.q_off[s];
+      const int ntiles = L > 0 ? (L * p.G + PF_ROWS - 1) / PF_ROWS : 0;
+      int n = 0;
+      for (int t = lane; t < ntiles; t += 64) n += tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
+      n = __builtin_amdgcn_readlane(wave_inclusive_scan(n), 63);
+      if (lane == 0) { seq_tiles[i] = ntiles; seq_items[i] = n; }
     }
+    __syncthreads();
     int ttotal, itotal;
-    const int tex = block_exclusive_scan(ntiles, sh, ttotal) + tcarry;
-    const int iex = block_exclusive_scan(nitems, sh, itotal) + icarry;
+    const int ntl = tid < nchunk ? seq_tiles[tid] : 0, nit = tid < nchunk ? seq_items[tid] : 0;
+    const int tex = block_exclusive_scan(ntl, sh, ttotal) + tcarry;
+    const int iex = block_exclusive_scan(nit, sh, itotal) + icarry;
+    if (tid < nchunk) { seq_tex[tid] = tex; seq_iex[tid] = iex; }
+    __syncthreads();
     // tile records heaviest first, each with its block of partial slots;
     // items split-major (every tile's split 0, then split 1, ...) so that
-    // workgroups running together read the same keys
-    int slot = iex, maxns = 0;
-    for (int k = 0; k < ntiles; ++k) {
-      const int t = ntiles - 1 - k;
-      const int ns = tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
-      if (tex + k < p.pf_tile_cap) p.pf_tiles[tex + k] = make_int4(s, t, slot, ns);
-      slot += ns;
-      maxns = max(maxns, ns);
-    }
-    int it = iex;
-    for (int ks = 0; ks < maxns; ++ks) {
-      int first = iex;
-      for (int k = 0; k < ntiles; ++k) {
+    // workgroups running together read the same keys: item (k, ks) goes to
+    // the sequence's first item + the items of all splits below ks + the
+    // tiles before k with more than ks splits
+    for (int i = wv; i < nchunk; i += 16) {
+      const int s = base + i;
+      const int L = p.qsl[s + 1] - p.qsl[s], ctx = p.ctx_lens[s], off = p.q_off[s];
+      const int ntiles = seq_tiles[i], t0x = seq_tex[i], i0x = seq_iex[i];
+      int slot = i0x, maxns = 0;
+      for (int k0 = 0; k0 < ntiles; k0 += 64) {
+        const int k = k0 + lane;
         const int t = ntiles - 1 - k;
-        const int ns = tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys);
-        if (ks < ns) {
-          if (it < p.pf_item_cap) p.pf_items[it] = make_int4(s, t, ks, first + ks);
-          ++it;
+        const int ns = k < ntiles ? tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys) : 0;
+        const int incl = wave_inclusive_scan(ns);
+        if (k < ntiles && t0x + k < p.pf_tile_cap) p.pf_tiles[t0x + k] = make_int4(s, t, slot + incl - ns, ns);
+        slot += __builtin_amdgcn_readlane(incl, 63);
+        maxns = max(maxns, ns);
+      }
+      for (int o = 32; o > 0; o >>= 1) maxns = max(maxns, __shfl_xor(maxns, o));
+      int below = 0;  // items of the splits below ks
+      for (int ks = 0; ks < maxns; ++ks) {
+        int before = 0, sslot = i0x;  // tiles before this chunk with > ks splits; their partial slots
+        for (int k0 = 0; k0 < ntiles; k0 += 64) {
+          const int k = k0 + lane;
+          const int t = ntiles - 1 - k;
+          const int ns = k < ntiles ? tile_splits(t, L, p.G, ctx, off, p.window, p.pf_split_keys) : 0;
+          const int has = ns > ks ? 1 : 0;
+          const int hincl = wave_inclusive_scan(has);
+          const int sincl = wave_inclusive_scan(ns);
+          const int it = i0x + below + before + hincl - has;
+          if (has && it < p.pf_item_cap) p.pf_items[it] = make_int4(s, t, ks, sslot + sincl - ns + ks);
+          before += __builtin_amdgcn_readlane(hincl, 63);
+          sslot += __builtin_amdgcn_readlane(sincl, 63);
         }
-        first += ns;
+        below += before;
       }
     }
     tcarry += ttotal;
     icarry += itotal;
+    __syncthreads();  // the shared per-sequence arrays are refilled by the next chunk
   }
   for (int i = tcarry + tid; i < p.pf_tile_cap; i += 1024) p.pf_tiles[i] = make_int4(-1, 0, 0, 0);
   for (int i = icarry + tid; i < p.pf_item_cap; i += 1024) p.pf_items[i] = make_int4(-1, 0, 0, 0);
