@@ -203,6 +203,19 @@ def test_nan_in_unused_slots_does_not_leak(d):
     _check_all(st, out, "nan tails")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_nan_tails_decode_only(d):
+    """A decode-only step (the decode-only launch, its splits and the
+    combine): NaN in partial-page tails and in unreferenced pages stays
+    masked, also for sequences of one to three pages."""
+    st = Step([(17, 1), (33, 1), (4097, 1), (1, 1), (48, 1), (49, 1), (2000, 1)], 16, 4, d, "bf16", seed=9,
+              fill=float("nan"))
+    kc, vc = st.upload()
+    out = st.run(kc, vc)
+    assert torch.isfinite(out.float()).all()
+    _check_all(st, out, "nan tails decode-only")
+
+
 @pytest.mark.parametrize("with_prefill", [False, True])
 def test_long_decode_splits_match_oracle(with_prefill):
     """256 decode sequences, two of them long (1,025 and 1,000 pages): with
