@@ -726,6 +726,34 @@ __device__ __forceinline__ void pf_dma(uint8_t* st, const Params& p, const int* 
 // Wait for this wave's LDS copies (vmcnt 0; the other counters untouched).
 __device__ __forceinline__ void wait_lds_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Once wave w's copy of a tile has landed: the V tokens of its page outside
+// [lo, hi) (page-relative; wave-uniform) are zeroed in the LDS stage.  The
+// copy brings whatever the page holds past the context end (and, under a
+// window, below the tile's floor); P is 0 there, but 0 * NaN is not, and
+// zeroing them here once keeps the P V product free of per-tile masks.
+// V rows are 32 bytes (one dim, 16 tokens); physical half ph of row r holds
+// tokens 8 (ph ^ r[3]) .. +7.
+template <int D>
+__device__ __forceinline__ void pf_zero_v(uint8_t* st, int w, int lane, int lo, int hi) {
+  uint8_t* vp = st + PfLds<D>::K_BYTES + w * 32 * D;
+#pragma unroll
+  for (int r0 = 0; r0 < D; r0 += 64) {
+    const int r = r0 + lane;
+    const int f = (r >> 3) & 1;
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      uint4* a = reinterpret_cast<uint4*>(vp + r * 32 + 16 * ph);
+      const int e = 8 * (ph ^ f);  // first token of this half
+      uint4 x = *a;
+      x.x = drop16(keep16(x.x, e + 0, hi), e + 0, lo);
+      x.y = drop16(keep16(x.y, e + 2, hi), e + 2, lo);
+      x.z = drop16(keep16(x.z, e + 4, hi), e + 4, lo);
+      x.w = drop16(keep16(x.w, e + 6, hi), e + 6, lo);
+      *a = x;
+    }
+  }
+}
+
 // Order of the N LDS fragment reads and the N MFMAs that take them, one each
 // (scheduler groups), in batches of R: the next batch's reads go out right
 // after the first MFMA of the current one.  While LDS copies are in flight
@@ -841,7 +869,16 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
   float m = -INFINITY, l = 0.f;
   const float c = p.scale_log2;
 
+  // this wave's page of tile kt, just landed in `st`: zero the V tokens no
+  // row of the tile may see (only on the tile that holds the context end, or
+  // under a window the one that holds the floor)
+  auto fix_tile = [&](int kt, uint8_t* st) {
+    const int kb = kt * PF_KEYS + 16 * wu;
+    const int hi = ctx - kb, lo = WIN ? kfloor - kb : 0;
+    if (hi < 16 || (WIN && lo > 0)) pf_zero_v<D>(st, wu, lane, lo, hi);
+  };
   wait_lds_copies();
+  if (kt0 < kt1) fix_tile(kt0, stage0);
   __syncthreads();
   auto tile_step = [&](int kt, const uint8_t* cur) {
     const int kbase = kt * PF_KEYS;
@@ -904,12 +941,10 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
       // for the same keys as one contiguous 16-byte load.  The row sum is
       // taken from the same bf16 P (a two-term dot product with ones per
       // packed pair), so the normaliser weighs exactly what P V does.
+      // V tokens past the context end (or below the window floor) were
+      // zeroed in LDS when their tile landed (pf_zero_v)
       float rsum[2] = {0.f, 0.f};
-      // MASKV: V tokens at or past the context end, or below the tile's
-      // first key, are zeroed as they are read (the copy brings whatever the
-      // page holds there; P is 0 for them, but 0 * NaN is not)
-      auto pv = [&](auto maskv) {
-        constexpr bool MASKV = decltype(maskv)::value;
+      {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -921,31 +956,14 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
                                         pack_bf16x2(sc[sub][r0 + 6], sc[sub][r0 + 7]));
             rsum[half] = sum_bf16x8(pb, rsum[half]);
             const uint8_t* vpage = vl + (2 * sub + half) * D * Lds::VROW;
-            const int k8 = kbase + (2 * sub + half) * 16 + 8 * gg;  // key of this lane's first V token
 #pragma unroll
             for (int dt = 0; dt < NO; ++dt) {
-              uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + vhalf);
-              if constexpr (MASKV) {
-                const int n = ctx - k8;
-                va.x = keep16(va.x, 0, n);
-                va.y = keep16(va.y, 2, n);
-                va.z = keep16(va.z, 4, n);
-                va.w = keep16(va.w, 6, n);
-                if (WIN) {
-                  const int nlo = kfloor - k8;
-                  va.x = drop16(va.x, 0, nlo);
-                  va.y = drop16(va.y, 2, nlo);
-                  va.z = drop16(va.z, 4, nlo);
-                  va.w = drop16(va.w, 6, nlo);
-                }
-              }
+              const uint4 va = *reinterpret_cast<const uint4*>(vpage + (32 * dt + l32) * Lds::VROW + vhalf);
               o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb), o[dt], 0, 0, 0);
             }
           }
         if constexpr (CB_PF_READAHEAD > 0) pf_read_schedule<4 * NO>();  // V fragments likewise
-      };
-      if (kbase + PF_KEYS > ctx || (WIN && kbase < kfloor)) pv(std::true_type{});
-      else pv(std::false_type{});
+      }
       l += rsum[0] + rsum[1];
     }
   };
@@ -956,11 +974,13 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
     if (kt + 1 < kt1) pf_dma<D>(stage1, p, pids, kt + 1, kt0, kvh, wu, od);
     tile_step(kt, stage0);
     wait_lds_copies();
+    if (kt + 1 < kt1) fix_tile(kt + 1, stage1);
     __syncthreads();
     if (kt + 1 >= kt1) break;
     if (kt + 2 < kt1) pf_dma<D>(stage0, p, pids, kt + 2, kt0, kvh, wu, od);
     tile_step(kt + 1, stage1);
     wait_lds_copies();
+    if (kt + 2 < kt1) fix_tile(kt + 2, stage0);
     __syncthreads();
   }
 
