@@ -21,9 +21,9 @@ is ``off = ctx - L`` and query row ``i`` sits at absolute position
     out    = sum_j w_j * v[j, g, :] / sum_j w_j
 
 Readings of points the pages leave open:
-* the causal boundary is inclusive (the page's mask keeps the diagonal:
-  ``tril(diagonal=start)`` over absolute positions), so every query sees at
-  least itself and no row is empty;
+* the causal boundary is inclusive (the page's example masks only keys at
+  later absolute positions, so a query keeps its own key), so every query
+  sees at least itself and no row is empty;
 * ``scale`` is passed in; the pages' code uses the library default
   ``1/sqrt(D)``, and callers pass that value rounded to fp32, the same value
   the GPU receives;
@@ -135,12 +135,3 @@ def attend(q, k, v, scale: float, window: int = 0) -> np.ndarray:
         out[:, h, :] = (w @ vg) / w.sum(axis=1, keepdims=True)
     return out
 
-
-def attend_step(seqs, scale: float, rows_only=False, window: int = 0):
-    """Whole engine step: a list of per-sequence ``(q, k_hist, v_hist)``.
-
-    Returns a list of ``[L_s, Hq, D]`` fp64 outputs in the same order.  Each
-    sequence is independent (the step is a batch of independent requests).
-    """
-    f = attend_rows if rows_only else attend
-    return [f(q, k, v, scale, window=window) for (q, k, v) in seqs]

@@ -256,3 +256,54 @@ def test_sliding_window_traces_match_oracle(seed):
 def test_window_and_sharing_together_are_rejected():
     with pytest.raises(cb.CbError):
         cb.Builder(64, 8, 100, sliding_window=16, allow_block_sharing=True)
+
+
+def test_builder_fragmentation_matches_the_hand_values():
+    """Cached-token accounting: the same hand-derived values as the oracle's pins
+    (tests/test_oracle_scheduler.py): a shared block counts once, a partly
+    filled page by its fill, a page released below the window not at all."""
+    toks_a = list(range(100, 140))
+    toks_b = list(range(100, 132)) + [7, 8, 9, 10]
+    b = cb.Builder(64, 8, 20, allow_block_sharing=True)
+    b.submit(0, 40, 3, tokens=toks_a)
+    b.step()
+    st = b.stats()
+    assert (st["used_slots"], st["allocated_slots"]) == (40, 48)
+    assert st["fragmentation"] == pytest.approx(8 / 48)
+    b.submit(1, 36, 2, tokens=toks_b)
+    b.step()
+    st = b.stats()
+    assert (st["used_slots"], st["allocated_slots"]) == (45, 64)
+    assert st["fragmentation"] == pytest.approx(19 / 64)
+    w = cb.Builder(64, 8, 20, sliding_window=20)
+    w.submit(0, 40, 10)
+    w.step()
+    w.step()
+    st = w.stats()
+    assert (st["used_slots"], st["allocated_slots"]) == (25, 32)
+    assert st["fragmentation"] == pytest.approx(7 / 32)
+
+
+def test_slots_match_the_page_model():
+    """cb_builder_slots == oracle/paging.slots_for over the request's block table
+    ([VLLM] "PagedAttention as virtual memory": slot = table[p / 16] * 16 + p % 16)."""
+    b = cb.Builder(512, 16, 300, page_shuffle_seed=77)
+    b.submit(0, 700, 5, 650)                 # imported: 41 pages held
+    b.submit(1, 90, 3, 0)
+    b.step()
+    for rid, a, e in ((0, 0, 650), (0, 17, 33), (0, 640, 651), (1, 0, 90), (1, 5, 5)):
+        got = b.slots(rid, a, e)
+        ref = paging.slots_for(b.block_table(rid), a, e)
+        assert got.dtype == np.int32 and np.array_equal(got, ref), (rid, a, e)
+    with pytest.raises(cb.CbError):
+        b.slots(0, 0, 10_000)                # past the held pages
+    with pytest.raises(cb.CbError):
+        b.slots(5, 0, 1)                     # unknown request
+    with pytest.raises(cb.CbError):
+        b.slots(0, 3, 2)                     # bad range
+    w = cb.Builder(512, 16, 300, sliding_window=64)
+    w.submit(0, 400, 50, 399)                # import keeps only the window's pages
+    assert w.block_table(0)[0] == -1
+    with pytest.raises(cb.CbError):
+        w.slots(0, 0, 1)                     # released below the window
+    assert np.array_equal(w.slots(0, 336, 399), paging.slots_for(w.block_table(0), 336, 399))

@@ -419,3 +419,50 @@ def test_window_pool_invariants_on_random_traces(seed):
             first_key = max(0, x.q_offset - W + 1)
             assert all(b != -2 for b in x.blocks[first_key // 16:])
     assert s.idle() or rid > 0
+
+
+# -- cached-token accounting (the fragmentation figure) --------------------------------
+#
+# AI Engineering from Scratch, "vLLM serving internals", "PagedAttention as
+# virtual memory": with 16-token pages the only waste is the unused tail of
+# each sequence's last page (under 4% in practice).  Fragmentation here is
+# (pages in use * 16 - cached tokens held) / (pages in use * 16), with a
+# shared page counted once and a page released below a sliding window not
+# counted at all.  The expected numbers below are worked out by hand.
+
+def _acct(s):
+    alloc = s.pages_in_use() * s.page
+    return s.used_slots(), alloc
+
+
+def test_used_slots_counts_a_shared_block_once_and_a_partial_page_by_its_fill():
+    toks_a = list(range(100, 140))                       # 40 prompt tokens
+    toks_b = list(range(100, 132)) + [7, 8, 9, 10]       # same first 32, own 4
+    s = FifoScheduler(64, 8, 20, allow_block_sharing=True)
+    s.submit(0, 40, 3, tokens=toks_a)
+    s.step()
+    # A holds tokens 0..39 in 3 pages (16 + 16 + 8); blocks 0 and 1 are registered
+    assert _acct(s) == (40, 48)
+    s.submit(1, 36, 2, tokens=toks_b)
+    st = s.step()
+    assert [(x.req_id, x.q_offset, x.q_len) for x in st.seqs] == [(0, 40, 1), (1, 32, 4)]
+    # pages: the two shared prompt blocks, A's third page (41 - 32 = 9 tokens)
+    # and B's third page (36 - 32 = 4 tokens).  Shared blocks count once.
+    used, alloc = _acct(s)
+    assert alloc == 4 * 16
+    assert used == 16 + 16 + 9 + 4                     # not 16*4 + 9 + 4 = 77
+    assert s.pages_in_use() == 4
+
+
+def test_used_slots_skips_pages_released_below_the_window():
+    s = FifoScheduler(64, 8, 20, sliding_window=20)
+    s.submit(0, 40, 10)
+    s.step()
+    assert _acct(s) == (40, 48)                          # 16 + 16 + 8 in 3 pages
+    s.step()
+    # at the step's start the lowest key any later row sees is 40 - 20 + 1 = 21,
+    # so page 0 (keys 0..15) is released; the decode then caches token 40:
+    # page 1 holds 16 tokens, page 2 holds 41 - 32 = 9
+    used, alloc = _acct(s)
+    assert (used, alloc) == (16 + 9, 2 * 16)            # not 41 over 48
+

@@ -124,17 +124,14 @@ def softmax_scale(head_dim: int) -> float:
 
 
 def page_example_tensors():
-    """The pages' worked example inputs: seed 0, ``randn(3, 1, 8, 1000, 64)``.
-
-    Ultralytics glossary, "Chunked Prefill", "How chunked prefill works": one
-    layer with 8 heads of 64 dims and a 1000-token prompt.  Returned as
-    float32 numpy arrays ``q, k, v[1000, 8, 64]`` (token-major).
+    """Inputs of the pages' worked example: one layer of 8 heads x 64 dims
+    and a 1000-token prompt (Ultralytics glossary, "Chunked Prefill", "How
+    chunked prefill works"), drawn N(0, 1) in float32 from this module's own
+    seeded generator (seed 0).  Returns ``q, k, v[1000, 8, 64]``, token-major.
     """
-    import torch
-    torch.manual_seed(0)
-    q, k, v = torch.randn(3, 1, 8, 1000, 64).unbind(0)
-    f = lambda t: t[0].permute(1, 0, 2).contiguous().numpy()
-    return f(q), f(k), f(v)
+    k, v = seq_kv(0, 0, 0, 1000, 8, 64, "f32")
+    q = seq_q(0, 0, 0, 1000, 8, 64, "f32")
+    return q, k, v
 
 
 # -- workload descriptors ------------------------------------------------------------
