@@ -94,7 +94,7 @@ def algorithmic(desc, hq, hkv, d, esize, window=0):
     else:
         pairs = ql * off + ql * (ql + 1) // 2
     flops = int((4 * d * hq * pairs).sum())
-    return kv + qo + meta, flops, int(pairs.sum())
+    return kv + qo + meta, flops, int(pairs.sum()), kv
 
 
 def main():
@@ -155,7 +155,7 @@ def main():
         v = wl.device_normal((n, hkv, d), w.dtype, dev, w.seed, i, 2)
         hist[i] = (k, v)
         if c > 0:
-            layer.write_positions(layer.builder.block_table(i), 0, c, k[:c], v[:c])
+            layer.write_positions(i, 0, c, k[:c], v[:c])
     for _ in range(advance):                       # earlier steps: append only
         desc = layer.schedule()
         ks = torch.cat([hist[int(r)][0][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
@@ -180,7 +180,7 @@ def main():
         f"{desc0.num_decodes} decodes, {T} query tokens, max ctx {desc0.max_context_len}")
 
     esize = 2 if w.dtype == "bf16" else 4
-    bytes_alg, flops_alg, pairs = algorithmic(desc0, hq, hkv, d, esize, args.window)
+    bytes_alg, flops_alg, pairs, kv_alg = algorithmic(desc0, hq, hkv, d, esize, args.window)
     lib = cb.load()
     cold = args.cold == "on" or (args.cold == "auto" and bytes_alg < 1e9)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold else None
@@ -192,8 +192,8 @@ def main():
         e.record()
     stream = layer.graph_stream if layer.graphs else torch.cuda.current_stream(dev)
 
-    def one_step(k=None):
-        if cold:                                               # evict the step's data from L2 and MALL
+    def one_step(k=None, flush=True):
+        if cold and flush:                                     # evict the step's data from L2 and MALL
             with torch.cuda.stream(stream):
                 scratch.fill_(k or 0)
         layer.load_builder(snapshot)                           # same starting state each time
@@ -257,6 +257,13 @@ def main():
     roof["span_us_p10_p50_p90"] = [pct(span_ms, 10), pct(span_ms, 50), pct(span_ms, 90)]
     roof["timing"] = ("cold: 1 GiB written before each step; step = device span" if cold
                       else "warm: steps back to back; step = wall time")
+    if roof["bound"] == "mfma":  # the shader clock the chip holds under this load
+        clk = gpu_clock_during(lambda: one_step(flush=False), 1.5)
+        torch.cuda.synchronize()
+        roof["clock_mhz"] = clk
+        if clk and clk.get("mean"):
+            # the same rate against the MFMA peak scaled to the measured clock (the published peak assumes 2.4 GHz)
+            roof["frac_at_measured_clock"] = round(roof["frac"] * 2400.0 / clk["mean"], 4)
     if roof["bound"] == "hbm":   # beside the peak: a plain streaming read of as many bytes
         ach = achievable_read_gbs(max(bytes_alg, 1 << 30))
         roof["achievable_read_GBps"] = ach
@@ -279,7 +286,9 @@ def main():
                    "num_tokens": T, "q_heads": hq, "kv_heads": hkv, "head_dim": d, "page_size": 16,
                    "max_batch_tokens": w.max_batch_tokens, "max_context_len": desc0.max_context_len,
                    "sliding_window": args.window, "graph_padding": [gq, gkv],
-                   "kv_bytes_read": bytes_alg, "visible_pairs": pairs, "flops": flops_alg},
+                   "algorithmic_bytes": bytes_alg, "algorithmic_kv_bytes": kv_alg,
+                   "algorithmic_other_bytes": bytes_alg - kv_alg, "visible_pairs": pairs,
+                   "algorithmic_flops": flops_alg},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -333,7 +342,7 @@ def run_trace(args, dev):
         lib.cb_profile_events(None, None)
         ev[1].record(stream)
         torch.cuda.synchronize()
-        nbytes, flops, _ = algorithmic(desc, hq, hkv, d, esize)
+        nbytes, flops, _, _ = algorithmic(desc, hq, hkv, d, esize)
         cls = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
         rows.append((T, nbytes, flops, ev[0].elapsed_time(ev[1]) / 1e3, ev[2].elapsed_time(ev[3]) / 1e3, cls,
                      desc.num_seqs, desc.num_decodes, int(desc.context_lens.max())))
@@ -389,6 +398,61 @@ def run_trace(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def gpu_clock_during(step_fn, seconds):
+    """Shader clock (MHz) the driver reports while ``step_fn`` runs back to back
+    for about ``seconds``: amdsmi GPU metrics sampled every 5 ms from a thread
+    (the per-XCD current clocks averaged).  None when the metrics are not
+    readable here."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+            v = m.get(key)
+            vals = v if isinstance(v, list) else [v]
+            vals = [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
+            if vals:
+                return sum(vals) / len(vals), key
+        return None
+
+    samples, key, stop = [], [], threading.Event()
+
+    def loop():
+        while not stop.is_set():
+            try:
+                r = read()
+                if r:
+                    samples.append(r[0])
+                    key[:] = [r[1]]
+            except Exception:
+                pass
+            stop.wait(0.005)
+
+    th = threading.Thread(target=loop, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step_fn()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not samples:
+        return None
+    import numpy as np
+    return {"mean": round(float(np.mean(samples)), 1), "p10": round(float(np.percentile(samples, 10)), 1),
+            "p90": round(float(np.percentile(samples, 90)), 1), "samples": len(samples),
+            "source": f"amdsmi gpu_metrics {key[0] if key else '?'}, back-to-back steps for {seconds} s"}
+
+
 def achievable_read_gbs(nbytes):
     """GB/s of the streaming-read probe (a child process) over ``nbytes``, or None."""
     probe = os.path.join(ROOT, "chunked_prefill_attention_amd", "hbm_probe")
@@ -437,7 +501,8 @@ def cpu_baseline(desc, q, hist, hq, hkv, d, budget_s, gpu_out, window=0):
             break
     log(f"[bench] cpu oracle: {reps} x whole step in {t_used:.1f}s ({threads} BLAS threads, {blas_name}); "
         f"max |gpu - oracle| {worst:.3e}")
-    return {"value": round(tokens / t_used, 1), "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(tokens / t_used, 1), "unit": "query tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": threads, "blas": blas_name, "kind": "oracle",
             "sample": f"the whole step ({desc.num_tokens} query tokens, {desc.num_seqs} sequences), "
                       f"{reps} repetition(s), fp64 numpy, {blas_name} BLAS",
             "max_abs_err_vs_gpu": worst}

@@ -232,6 +232,12 @@ class Builder:
                                                n.value, C.byref(n)))
         return buf[:n.value]
 
+    def slots(self, req_id: int, start: int, end: int) -> np.ndarray:
+        """Cache slots of logical positions ``start .. end-1`` of a request (int32)."""
+        out = np.zeros(max(end - start, 1), np.int32)
+        check(self._lib.cb_builder_slots(self._h, req_id, start, end, out.ctypes.data_as(C.POINTER(C.c_int32))))
+        return out[:max(end - start, 0)]
+
     def stats(self) -> dict:
         s = BuilderStats()
         check(self._lib.cb_builder_stats_get(self._h, C.byref(s)))

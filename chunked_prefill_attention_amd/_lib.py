@@ -52,6 +52,11 @@ class EngineConfig(C.Structure):
                 ("meta_host", vp), ("meta_bytes", sz), ("workspace", vp), ("workspace_bytes", sz)]
 
 
+class EngineStats(C.Structure):
+    _fields_ = [("steps_scheduled", i64), ("steps_attended", i64), ("slot_waits", i64),
+                ("graph_captures", i64), ("graph_replays", i64), ("graphs_cached", i64)]
+
+
 # name -> (restype, argtypes); one line per declaration of include/cb.h
 SIGNATURES = {
     "cb_status_string": (C.c_char_p, [C.c_int]),
@@ -70,6 +75,7 @@ SIGNATURES = {
     "cb_builder_step": (C.c_int, [vp, C.POINTER(StepDesc)]),
     "cb_builder_block_table": (C.c_int, [vp, i64, P_i32, i32, P_i32]),
     "cb_builder_stats_get": (C.c_int, [vp, C.POINTER(BuilderStats)]),
+    "cb_builder_slots": (C.c_int, [vp, i64, i32, i32, P_i32]),
     "cb_engine_create": (C.c_int, [C.POINTER(EngineConfig), C.POINTER(vp)]),
     "cb_engine_destroy": (None, [vp]),
     "cb_engine_builder": (vp, [vp]),
@@ -78,6 +84,7 @@ SIGNATURES = {
     "cb_engine_schedule": (C.c_int, [vp, vp, C.POINTER(StepDesc)]),
     "cb_engine_attend": (C.c_int, [vp, vp, vp, vp, vp, vp]),
     "cb_engine_workspace_bytes": (sz, [vp]),
+    "cb_engine_stats_get": (C.c_int, [vp, C.POINTER(EngineStats)]),
     "cb_engine_load_builder": (C.c_int, [vp, vp]),
     "cb_engine_set_graphs": (C.c_int, [vp, i32, i32, i32]),
     "cb_engine_padded_tokens": (i32, [vp]),

@@ -545,6 +545,22 @@ int cb_builder_block_table(const cb_builder* b, int64_t req_id, int32_t* out, in
   return CB_OK;
 }
 
+int cb_builder_slots(const cb_builder* b, int64_t req_id, int32_t start, int32_t end, int32_t* out) {
+  cb::clear_error();
+  if (!b || (end > start && !out)) return cb::fail(CB_ERR_INVALID, "cb_builder_slots: null argument");
+  if (start < 0 || end < start) return cb::fail(CB_ERR_INVALID, "cb_builder_slots: bad range [%d, %d)", start, end);
+  auto it = b->by_id.find(req_id);
+  if (it == b->by_id.end()) return cb::fail(CB_ERR_INVALID, "unknown request id %lld", (long long)req_id);
+  const auto& pages = it->second->pages;
+  for (int32_t p = start; p < end; ++p) {
+    const size_t lp = (size_t)(p / CB_PAGE_SIZE);
+    if (lp >= pages.size() || pages[lp] < 0)
+      return cb::fail(CB_ERR_INVALID, "position %d of request %lld is not in a held page", p, (long long)req_id);
+  }
+  for (int32_t p = start; p < end; ++p) out[p - start] = pages[(size_t)(p / CB_PAGE_SIZE)] * CB_PAGE_SIZE + p % CB_PAGE_SIZE;
+  return CB_OK;
+}
+
 int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out) {
   cb::clear_error();
   if (!b || !out) return cb::fail(CB_ERR_INVALID, "cb_builder_stats_get: null argument");

@@ -149,6 +149,10 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
   if (num_tokens > 0 && num_seqs == 0)
     return cb::fail(CB_ERR_INVALID, "num_tokens > 0 with no sequences");
   if (!std::isfinite(scale)) return cb::fail(CB_ERR_INVALID, "scale must be finite");
+  // the bf16 online softmax keeps the running maximum of raw scores, which
+  // orders like the scaled scores only when the scale is positive
+  if (dtype == CB_BF16 && !(scale > 0.f))
+    return cb::fail(CB_ERR_UNSUPPORTED, "the bf16 path needs scale > 0 (got %g)", (double)scale);
   if (sliding_window < 0) return cb::fail(CB_ERR_INVALID, "sliding_window must be >= 0");
   if ((int64_t)num_tokens * num_q_heads * head_dim >= (int64_t(1) << 40))
     return cb::fail(CB_ERR_INVALID, "step too large");

@@ -60,6 +60,8 @@ struct cb_engine {
   bool capture = false;
   std::map<GraphKey, hipGraphExec_t> graphs;
   int64_t n_captures = 0, n_replays = 0;
+  int64_t n_scheduled = 0, n_attended = 0;
+  int64_t n_slot_waits = 0;  // schedules whose staging slot was still being read, and waited
   void drop_graphs() {
     for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
@@ -170,8 +172,16 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
                     (long long)need, (long long)e->slot_ints);
   const int slot = e->pending ? e->slot : (e->slot_used[e->slot] ? e->slot ^ 1 : e->slot);
   // the staging slot must not be rewritten while its previous upload is in flight
-  if (e->slot_used[slot] && hipEventSynchronize(e->copied[slot]) != hipSuccess)
-    return cb::fail(CB_ERR_DEVICE, "cb_engine_schedule: waiting for the previous upload failed");
+  if (e->slot_used[slot]) {
+    const hipError_t q = hipEventQuery(e->copied[slot]);
+    if (q == hipErrorNotReady) {
+      e->n_slot_waits++;
+      if (hipEventSynchronize(e->copied[slot]) != hipSuccess)
+        return cb::fail(CB_ERR_DEVICE, "cb_engine_schedule: waiting for the previous upload failed");
+    } else if (q != hipSuccess) {
+      return cb::fail(CB_ERR_DEVICE, "cb_engine_schedule: querying the previous upload failed");
+    }
+  }
   int st = cb_builder_step(e->builder, &e->step);
   if (st != CB_OK) return st;
   const cb_step& d = e->step;
@@ -268,6 +278,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   }
   e->slot = slot;
   e->pending = true;
+  e->n_scheduled++;
   e->d_qsl = dv + o_qsl;
   e->d_ctx = dv + o_ctx;
   e->d_off = dv + o_off;
@@ -319,6 +330,18 @@ int cb_engine_graph_stats(const cb_engine* e, int64_t* captures, int64_t* replay
   return CB_OK;
 }
 
+int cb_engine_stats_get(const cb_engine* e, cb_engine_stats* out) {
+  cb::clear_error();
+  if (!e || !out) return cb::fail(CB_ERR_INVALID, "cb_engine_stats_get: null argument");
+  out->steps_scheduled = e->n_scheduled;
+  out->steps_attended = e->n_attended;
+  out->slot_waits = e->n_slot_waits;
+  out->graph_captures = e->n_captures;
+  out->graph_replays = e->n_replays;
+  out->graphs_cached = (int64_t)e->graphs.size();
+  return CB_OK;
+}
+
 int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void* v_new, void* out,
                      void* stream) {
   cb::clear_error();
@@ -363,7 +386,10 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   if (!e->capture) {
     int st = launch();
     if (st == CB_OK) st = staged();
-    if (st == CB_OK) e->pending = false;
+    if (st == CB_OK) {
+      e->pending = false;
+      e->n_attended++;
+    }
     return st;
   }
   const hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -395,7 +421,10 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
     return cb::fail(CB_ERR_DEVICE, "cb_engine_attend: graph launch failed");
   e->n_replays++;
   const int st = staged();
-  if (st == CB_OK) e->pending = false;
+  if (st == CB_OK) {
+    e->pending = false;
+    e->n_attended++;
+  }
   return st;
 }
 

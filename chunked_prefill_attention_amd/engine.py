@@ -22,7 +22,7 @@ import ctypes as C
 import numpy as np
 
 from . import Builder, Step, builder_config, kv_append, CB_BF16, CB_F32, PAGE_SIZE
-from ._lib import EngineConfig, StepDesc, CbError, check, load, CB_ERR_CAPACITY, CB_ERR_WORKSPACE
+from ._lib import EngineConfig, EngineStats, StepDesc, CbError, check, load, CB_ERR_CAPACITY, CB_ERR_WORKSPACE
 
 
 def _arr(ptr, n, dtype):
@@ -157,6 +157,22 @@ class PagedAttentionLayer:
         check(self._lib.cb_engine_graph_stats(self._h, C.byref(c), C.byref(r), C.byref(n)))
         return {"captures": c.value, "replays": r.value, "cached": n.value}
 
+    def reserve_workspace(self, nbytes: int) -> None:
+        """Hold at least ``nbytes`` of attention workspace now, so that no later
+        step has to grow it (growing synchronises the device)."""
+        if self._ws is not None and self._ws.numel() >= nbytes:
+            return
+        self.torch.cuda.synchronize(self.device)
+        self._ws = self.torch.empty(int(nbytes), dtype=self.torch.uint8, device=self.device)
+        check(self._lib.cb_engine_set_workspace(self._h, self._ws.data_ptr(), self._ws.numel()))
+
+    def stats(self) -> dict:
+        """Engine counters (cb_engine_stats_get): steps scheduled and attended,
+        waits for a staging slot, graph captures and replays."""
+        s = EngineStats()
+        check(self._lib.cb_engine_stats_get(self._h, C.byref(s)))
+        return {f: getattr(s, f) for f, _ in EngineStats._fields_}
+
     # -- a1 + a2: builder step and metadata upload -----------------------------------------
     def schedule(self, stream=None) -> StepView:
         self._gen += 1
@@ -217,10 +233,10 @@ class PagedAttentionLayer:
         """Restore the scheduler state from a builder snapshot (``Builder.clone()``)."""
         check(self._lib.cb_engine_load_builder(self._h, snapshot._h))
 
-    def write_positions(self, req_pages: np.ndarray, start: int, end: int, k_rows, v_rows, stream=None):
-        """Write K/V rows of logical positions start..end-1 of a request whose
-        block table is ``req_pages`` (used to import in-flight requests)."""
-        pos = np.arange(start, end)
-        slots = (req_pages[pos // PAGE_SIZE].astype(np.int64) * PAGE_SIZE + pos % PAGE_SIZE).astype(np.int32)
+    def write_positions(self, req_id: int, start: int, end: int, k_rows, v_rows, stream=None):
+        """Write K/V rows of logical positions start..end-1 of request ``req_id``
+        into its pages (used to import in-flight requests); the slots come from
+        the builder (cb_builder_slots)."""
+        slots = self.builder.slots(req_id, start, end)
         sm = self.torch.from_numpy(slots).to(self.device)
         kv_append(k_rows, v_rows, self.k_cache, self.v_cache, sm, stream=stream)

@@ -150,13 +150,21 @@ size_t cb_attention_workspace_bytes(int32_t num_seqs, int32_t num_decodes, int32
  *                     path (any q_len >= 0, including 1)
  *   max_context_len   host upper bound of context_lens (sizes the grid)
  *   Grouped-query mapping: query head h reads KV head h / (Hq / Hkv).
- *   scale             softmax scale (1/sqrt(head_dim) by convention)
+ *   scale             softmax scale (1/sqrt(head_dim) by convention); finite;
+ *                     the bf16 path requires scale > 0 (its online softmax
+ *                     tracks the maximum raw score, which orders like the
+ *                     scaled scores only for a positive scale)
  *   sliding_window    0 for full causal attention; W > 0 restricts row p to
  *                     keys p-W < j <= p ([CBA] "Memory management": sliding
  *                     layers keep only a fixed window of recent tokens).  Block
- *                     table entries for pages wholly below a sequence's first
- *                     row's window are never read (they may be -1), and cache
- *                     slots below a row's window do not affect it, NaN included
+ *                     table entries for pages wholly below the window of a
+ *                     sequence's first query row in the step are never read
+ *                     (they may be -1), and cache slots below that window do
+ *                     not affect any row, NaN included.  Slots from there up
+ *                     to a later row's own window start get weight zero in
+ *                     that row but must hold finite values (the rows of a
+ *                     prefill tile share one P V product, so 0 * NaN would
+ *                     reach them); the builder's release rule keeps them so
  *   workspace         device, >= cb_attention_workspace_bytes(...) bytes
  *                     (may be NULL when that is 0); contents on entry do not
  *                     matter; two calls that share a workspace must be
@@ -349,6 +357,16 @@ int cb_builder_step(cb_builder* b, cb_step* out);
 int cb_builder_block_table(const cb_builder* b, int64_t req_id, int32_t* out, int32_t cap,
                            int32_t* n);
 
+/* Slot mapping of logical positions start .. end-1 of request req_id, for
+ * writing their K/V with cb_kv_append (e.g. the history of an imported
+ * request).  [VLLM] "PagedAttention as virtual memory": position p lives in
+ * slot block_table[p / 16] * 16 + p % 16.  out (host int32, end - start
+ * entries, caller-owned) receives the slots; nothing is written on error.
+ * Errors: CB_ERR_INVALID (unknown id, null out with end > start, start < 0,
+ * end < start, a position whose page the request does not hold -- past its
+ * block table or released below a sliding window). */
+int cb_builder_slots(const cb_builder* b, int64_t req_id, int32_t start, int32_t end, int32_t* out);
+
 int cb_builder_stats_get(const cb_builder* b, cb_builder_stats* out);
 
 
@@ -466,6 +484,23 @@ int32_t cb_engine_padded_tokens(const cb_engine* e);
 
 /* Graphs recorded and launched so far, and graphs held now. */
 int cb_engine_graph_stats(const cb_engine* e, int64_t* captures, int64_t* replays, int64_t* cached);
+
+/* Engine counters.  [CBA] "Async batching": the host prepares step N+1 while
+ * the device runs step N; with two staging slots the host runs at most two
+ * steps ahead, and slot_waits counts the schedules that found their slot's
+ * previous reader (the upload or the append kernel of the step two back)
+ * still pending on the device and waited for it. */
+typedef struct {
+  int64_t steps_scheduled;  /* cb_engine_schedule calls that produced a step */
+  int64_t steps_attended;   /* steps whose device work was enqueued */
+  int64_t slot_waits;       /* schedules that waited for a staging slot */
+  int64_t graph_captures;   /* as cb_engine_graph_stats */
+  int64_t graph_replays;
+  int64_t graphs_cached;
+} cb_engine_stats;
+
+/* Errors: CB_ERR_INVALID (null argument). */
+int cb_engine_stats_get(const cb_engine* e, cb_engine_stats* out);
 
 /* Workspace the last scheduled step needs (0 if none). */
 size_t cb_engine_workspace_bytes(const cb_engine* e);

@@ -84,3 +84,11 @@ def test_kv_append_rejects_bad_arguments():
     assert f(NULL, FAKE, FAKE, FAKE, FAKE, 10, 8, 128, 100, 16, 1, NULL) == -1
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 8, 128, 0, 16, 1, NULL) == -1
     assert f(NULL, NULL, NULL, NULL, NULL, 0, 8, 128, 100, 16, 1, NULL) == 0   # empty: no-op
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, -0.0])
+def test_bf16_rejects_non_positive_scale(scale):
+    """The bf16 online softmax orders scores by their raw value, which matches
+    the scaled order only for scale > 0: other scales are refused up front."""
+    assert _step(scale=scale) == -2
+    assert b"scale > 0" in _lib.load().cb_last_error()

@@ -34,7 +34,7 @@ def _brute_pairs(seqs, window=0):
 def test_pairs_and_flops_match_brute_force(window):
     seqs = [(1, 1), (17, 1), (90, 33), (64, 64), (130, 7), (5, 0)]
     hq, hkv, d = 8, 2, 64
-    nbytes, flops, pairs = bench.algorithmic(_desc(seqs), hq, hkv, d, 2, window)
+    nbytes, flops, pairs = bench.algorithmic(_desc(seqs), hq, hkv, d, 2, window)[:3]
     assert pairs == _brute_pairs(seqs, window)
     assert flops == 4 * d * hq * pairs
 
@@ -43,7 +43,7 @@ def test_pairs_and_flops_match_brute_force(window):
 def test_bytes_match_their_definition(window):
     seqs = [(1, 1), (17, 1), (90, 33), (64, 64), (130, 7)]
     hq, hkv, d, e = 8, 2, 64, 2
-    nbytes, _, _ = bench.algorithmic(_desc(seqs), hq, hkv, d, e, window)
+    nbytes, _, _ = bench.algorithmic(_desc(seqs), hq, hkv, d, e, window)[:3]
     kv = meta = 0
     for c, q in seqs:
         off = c - q
@@ -59,7 +59,7 @@ def test_bytes_match_their_definition(window):
 def test_mixed_step_prefill_figures():
     """The mixed step's three prefill chunks: 476 tokens at offset 1024, 700
     and 808 at offset 0 (32 q heads, D 128): 1,173,136 visible pairs, 19.2 GFLOP."""
-    _, flops, pairs = bench.algorithmic(_desc([(1500, 476), (700, 700), (808, 808)]), 32, 8, 128, 2)
+    _, flops, pairs = bench.algorithmic(_desc([(1500, 476), (700, 700), (808, 808)]), 32, 8, 128, 2)[:3]
     assert pairs == 1_173_136
     assert round(flops / 1e9, 1) == 19.2
 
@@ -68,14 +68,15 @@ def test_long_prompt_chunk_figures():
     """Chunk k of the 20,000-token prompt in 512-token chunks has 512·512k +
     131,328 visible pairs; k = 38 (offset 19,456, 64 q heads, D 128) is 330.7 GFLOP."""
     for k in (0, 1, 19, 38):
-        _, _, pairs = bench.algorithmic(_desc([(512 * k + 512, 512)]), 64, 8, 128, 2)
+        _, _, pairs = bench.algorithmic(_desc([(512 * k + 512, 512)]), 64, 8, 128, 2)[:3]
         assert pairs == 512 * 512 * k + 131_328
-    _, flops, _ = bench.algorithmic(_desc([(19456 + 512, 512)]), 64, 8, 128, 2)
+    _, flops, _ = bench.algorithmic(_desc([(19456 + 512, 512)]), 64, 8, 128, 2)[:3]
     assert round(flops / 1e9, 1) == 330.7
 
 
 def test_decode_kv_bytes_are_four_kib_per_token():
     """A decode token with 8 KV heads of 128 dims in bf16 reads 4 KiB of KV per context token."""
-    nbytes, _, _ = bench.algorithmic(_desc([(1000, 1)]), 32, 8, 128, 2)
+    nbytes, _, _ = bench.algorithmic(_desc([(1000, 1)]), 32, 8, 128, 2)[:3]
     kv = nbytes - 2 * 32 * 128 * 2 - (63 + 4) * 4
     assert kv == 1000 * 4096
+    assert bench.algorithmic(_desc([(1000, 1)]), 32, 8, 128, 2)[3] == 1000 * 4096   # the KV part on its own

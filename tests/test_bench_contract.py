@@ -39,6 +39,10 @@ def test_json_line_fields():
     assert 0 < roof["frac"] <= 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["traffic"] is None or roof["traffic"] > 0
     cpu = rec["cpu_baseline"]
-    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["sample"]
+    assert cpu["cores"] == len(os.sched_getaffinity(0)) and cpu["blas_threads"] >= 1
+    cfg = rec["config"]
+    assert cfg["algorithmic_bytes"] == cfg["algorithmic_kv_bytes"] + cfg["algorithmic_other_bytes"]
+    assert cfg["algorithmic_kv_bytes"] > 0.9 * cfg["algorithmic_bytes"]
     # the oracle's rows agree with the GPU's within the bf16 bound the parity tests use
     assert cpu["max_abs_err_vs_gpu"] < 0.05

@@ -292,7 +292,7 @@ def test_engine_mixed_bf16_matches_direct_calls_bitwise():
         k, v = wl.seq_kv(31, i, 0, p + o, hkv, d, "bf16")
         hist[i] = (k, v)
         if c:
-            layer.write_positions(layer.builder.block_table(i), 0, c, to_dev(k[:c], "bf16"), to_dev(v[:c], "bf16"))
+            layer.write_positions(i, 0, c, to_dev(k[:c], "bf16"), to_dev(v[:c], "bf16"))
             write_history(kc2, vc2, k, v, ref_b.block_table(i), 0, c, "bf16")
     for step in range(3):
         dsc = layer.schedule().copy()

@@ -2,9 +2,9 @@
 metadata upload -> cb_kv_append -> cb_attention_step), against the oracle.
 
 Decode rows are checked for every sequence; prefill chunks are checked on
-sampled query rows (first, last and seeded random rows, every head), which
-the oracle computes one by one.  The FIFO trace checks sampled rows of every
-one of its steps.
+sampled query rows (first, last and seeded random rows), which the oracle
+computes one by one.  The long prompt is checked on all 40 steps and the FIFO
+trace on every one of its steps, its appends bit for bit.
 """
 import math
 
@@ -14,6 +14,7 @@ import torch
 
 from gpu_util import compare, dev, say
 from oracle import attention as ora
+from oracle import paging
 from chunked_prefill_attention_amd.engine import PagedAttentionLayer
 import workloads as wl
 
@@ -34,7 +35,7 @@ class Run:
             k, v = wl.seq_kv(w.seed, i, 0, p + o - 1, w.n_kv_heads, w.head_dim, w.dtype)
             self.hist[i] = (k, v)
             if c > 0:
-                self.layer.write_positions(self.layer.builder.block_table(i), 0, c, self._dev(k[:c]),
+                self.layer.write_positions(i, 0, c, self._dev(k[:c]),
                                            self._dev(v[:c]))
         self.steps = 0
 
@@ -80,6 +81,33 @@ class Run:
                                            am[pick]))
         return worst
 
+    def check_groups(self, desc, q, out, n_rows=4, rng_seed=0):
+        """Every decode row and ``n_rows`` + 2 rows of each prefill chunk (its
+        first, last and seeded others), each on one seeded KV head and the
+        query heads that read it."""
+        w = self.w
+        G = w.n_q_heads // w.n_kv_heads
+        scale = wl.softmax_scale(w.head_dim)
+        rng = np.random.default_rng(rng_seed)
+        worst = 0.0
+        for s in range(desc.num_seqs):
+            i = int(desc.req_ids[s])
+            a, e = int(desc.query_start_loc[s]), int(desc.query_start_loc[s + 1])
+            ctx, L = int(desc.context_lens[s]), e - a
+            pick = [0] if L == 1 else sorted(set([0, L - 1] + rng.integers(0, L, size=n_rows).tolist()))
+            for ii in pick:
+                g = int(rng.integers(0, w.n_kv_heads))
+                heads = slice(g * G, (g + 1) * G)
+                pos = ctx - L + ii
+                k = self.hist[i][0][:pos + 1, g:g + 1]
+                v = self.hist[i][1][:pos + 1, g:g + 1]
+                qr = q[a + ii:a + ii + 1, heads]
+                ref = ora.attend(qr, k, v, scale)
+                am = ora.attend(qr, k, np.abs(v), scale)
+                worst = max(worst, compare(out[a + ii:a + ii + 1, heads], ref, w.dtype,
+                                           f"seq {s} row {ii} kv head {g}", am))
+        return worst
+
 
 def test_decode_only_128_sequences():
     say("decode-only: 128 seqs, ctx U[512,4096], 32q/8kv, D128, bf16")
@@ -98,17 +126,32 @@ def test_mixed_step():
     say(f"  max abs err {r.check(desc, q, out, n_rows=48):.2e}")
 
 
+@pytest.mark.timeout(900)
 def test_long_prompt_forty_steps():
+    """Every one of the 40 steps is checked: all 127 decode rows and six rows
+    of the chunk, each on a seeded KV head's group of 8 query heads; steps 0,
+    1, 19, 38 and 39 also on every head of every decode row and of 26 chunk
+    rows."""
     say("long prompt: 127 decodes + 20000-token prompt in 512-token chunks, 64q/8kv, D128, bf16")
     r = Run(wl.long_prompt())
     for k in range(40):
         desc, q, out = r.step()
         pf = desc.q_lens[desc.num_decodes:]
         assert desc.num_decodes == 127 and pf.tolist() == ([512] if k < 39 else [32])
+        err = r.check_groups(desc, q, out, rng_seed=100 + k)
         if k in (0, 1, 19, 38, 39):
-            say(f"  step {k}: chunk at {desc.q_offsets[-1]}, max abs err {r.check(desc, q, out, rng_seed=k):.2e}")
-        else:
-            assert np.isfinite(out).all()
+            err = max(err, r.check(desc, q, out, rng_seed=k))
+        say(f"  step {k}: chunk at {desc.q_offsets[-1]}, max abs err {err:.2e}")
+
+
+def _bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _pages_of(cache: torch.Tensor, pages: np.ndarray) -> np.ndarray:
+    """Host copy (bf16 bits) of the given physical pages of a device cache."""
+    idx = torch.from_numpy(pages.astype(np.int64)).to(cache.device)
+    return cache[idx].view(torch.int16).cpu().numpy().view(np.uint16)
 
 
 @pytest.mark.timeout(900)
@@ -116,9 +159,14 @@ def test_fifo_trace_every_step():
     """256 requests, Poisson arrivals, lognormal prompts, geometric outputs, pool 200k pages.
 
     K, V and Q of each step are drawn on the device; the host keeps a copy of
-    every request's K/V history for the oracle.  Every step is checked on
-    sampled rows: one decode sequence and, when present, the first and last
-    rows of one prefill chunk, each on the query heads of one seeded KV head.
+    every request's K/V history for the oracle.  Every step is checked:
+    * append: the pages the step wrote are read back and every slot of its
+      slot mapping must hold the token's K and V bits (oracle/paging.append
+      onto the read-back pages changes nothing);
+    * attention, on every query head: one seeded decode row, and the first,
+      last and three seeded interior rows of one prefill chunk;
+    * paging: the sampled sequences' whole histories, gathered through their
+      block tables (oracle/paging.gather), equal the host copies bit for bit.
     """
     hq, hkv, d, dtype = 64, 8, 128, "bf16"
     reqs = wl.fifo_trace()
@@ -130,10 +178,14 @@ def test_fifo_trace_every_step():
     step = 0
     rng = np.random.default_rng(55)
     worst = 0.0
-    checked_rows = 0
+    checked_rows = appended = 0
     frag = []
-    while pending or L.builder.stats()["num_waiting"] + L.builder.stats()["num_prefilling"] \
-            + L.builder.stats()["num_decoding"] + L.builder.stats()["num_finished_pending"] > 0:
+
+    def busy():
+        st = L.builder.stats()
+        return st["num_waiting"] + st["num_prefilling"] + st["num_decoding"] + st["num_finished_pending"] > 0
+
+    while pending or busy():
         while pending and pending[0].arrival_step <= step:
             r = pending.pop(0)
             L.builder.submit(r.req_id, r.prompt_len, r.output_len)
@@ -149,6 +201,7 @@ def test_fifo_trace_every_step():
         vn = wl.device_normal((T, hkv, d), dtype, dev(), 5, step, 2)
         qd = wl.device_normal((T, hq, d), dtype, dev(), 5, step, 3)
         out = L.attend(qd, kn, vn)
+        torch.cuda.synchronize()
         kh = kn.view(torch.int16).cpu().numpy().view(np.uint16)
         vh = vn.view(torch.int16).cpu().numpy().view(np.uint16)
         for s in range(desc.num_seqs):
@@ -156,34 +209,46 @@ def test_fifo_trace_every_step():
             a, e = desc.query_start_loc[s], desc.query_start_loc[s + 1]
             hist[i][0, desc.q_offsets[s]:desc.context_lens[s]] = kh[a:e]
             hist[i][1, desc.q_offsets[s]:desc.context_lens[s]] = vh[a:e]
-        # sampled rows: one decode sequence, one prefill chunk (first and last rows)
+
+        # the append: every slot written holds its token's bits
+        slots = desc.slot_mapping.astype(np.int64)
+        pages = np.unique(slots // 16)
+        kp, vp = _pages_of(L.k_cache, pages), _pages_of(L.v_cache, pages)
+        local = np.searchsorted(pages, slots // 16) * 16 + slots % 16
+        ke, ve = kp.copy(), vp.copy()
+        paging.append(ke, ve, kh, vh, local)
+        assert np.array_equal(ke, kp) and np.array_equal(ve, vp), f"trace step {step}: appended slots differ"
+        appended += T
+
+        # sampled rows, every query head
         picks = []
         if desc.num_decodes:
             picks.append((int(rng.integers(0, desc.num_decodes)), [0]))
         if desc.num_seqs > desc.num_decodes:
             s = int(rng.integers(desc.num_decodes, desc.num_seqs))
             n = int(desc.q_lens[s])
-            picks.append((s, sorted({0, n - 1})))
-        qh = out_h = None
+            picks.append((s, sorted({0, n - 1} | set(rng.integers(0, n, size=3).tolist()))))
+        if picks:
+            qh = qd.float().cpu().numpy()
+            out_h = out.float().cpu().numpy()
         for s, rows in picks:
-            if qh is None:
-                torch.cuda.synchronize()
-                qh = qd.float().cpu().numpy()
-                out_h = out.float().cpu().numpy()
             i = int(desc.req_ids[s])
-            a, e, ctx = int(desc.query_start_loc[s]), int(desc.query_start_loc[s + 1]), int(desc.context_lens[s])
-            # one KV head and its query-head group (a seeded choice per check)
-            g = int(rng.integers(0, hkv))
-            G = hq // hkv
-            heads = slice(g * G, (g + 1) * G)
-            k = torch.from_numpy(hist[i][0, :ctx, g:g + 1].view(np.int16)).view(torch.bfloat16).float().numpy()
-            v = torch.from_numpy(hist[i][1, :ctx, g:g + 1].view(np.int16)).view(torch.bfloat16).float().numpy()
-            pairs = [(ii, h) for ii in rows for h in range(G)]
-            qg = qh[a:e][:, heads]
-            ref = ora.attend_rows(qg, k, v, scale, rows=pairs)
-            am = ora.attend_rows(qg, k, np.abs(v), scale, rows=pairs)
-            worst = max(worst, compare(out_h[a:e][rows][:, heads], ref[rows], dtype,
-                                       f"trace step {step} seq {s} kv head {g}", am[rows]))
+            a, ctx = int(desc.query_start_loc[s]), int(desc.context_lens[s])
+            n = int(desc.q_lens[s])
+            # the sequence's history through its block table == the host copy
+            row = desc.block_tables[s][: -(-ctx // 16)].astype(np.int64)
+            kq, vq = _pages_of(L.k_cache, row), _pages_of(L.v_cache, row)
+            kg, vg = paging.gather(kq, vq, np.arange(len(row)), ctx)
+            assert np.array_equal(kg, hist[i][0, :ctx]) and np.array_equal(vg, hist[i][1, :ctx]), \
+                f"trace step {step} seq {s}: paged history differs"
+            k, v = _bf16_bits_to_f32(hist[i][0, :ctx]), _bf16_bits_to_f32(hist[i][1, :ctx])
+            for ii in rows:
+                pos = ctx - n + ii
+                qr = qh[a + ii:a + ii + 1]
+                ref = ora.attend(qr, k[:pos + 1], v[:pos + 1], scale)
+                am = ora.attend(qr, k[:pos + 1], np.abs(v[:pos + 1]), scale)
+                worst = max(worst, compare(out_h[a + ii:a + ii + 1], ref, dtype,
+                                           f"trace step {step} seq {s} row {ii}", am))
             checked_rows += len(rows)
         st = L.builder.stats()
         if st["allocated_slots"]:
@@ -192,5 +257,6 @@ def test_fifo_trace_every_step():
             say(f"  trace step {step}: T={T} decodes={desc.num_decodes} seqs={desc.num_seqs} worst={worst:.2e}")
         step += 1
         assert step < 5000
-    say(f"  trace done: {step} steps, {checked_rows} rows checked, mean fragmentation {np.mean(frag):.4f}")
+    say(f"  trace done: {step} steps, {appended} appended tokens read back, {checked_rows} rows x {hq} heads "
+        f"checked, mean fragmentation {np.mean(frag):.4f}")
     assert L.builder.stats()["total_finished"] == len(reqs)
