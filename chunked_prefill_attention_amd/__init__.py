@@ -20,7 +20,7 @@ import numpy as np
 from ._lib import (BuilderConfig, BuilderStats, CbError, StepDesc, check, load,
                    CB_F32, CB_BF16, CB_POLICY_FIFO, CB_POLICY_PREFILL_FIRST, PAGE_SIZE, LIB_PATH)
 
-__all__ = ["kv_append", "attention_step", "attention_workspace_bytes", "Builder", "Step", "builder_config",
+__all__ = ["kv_append", "attention_step", "attention_step_noalloc", "attention_workspace_bytes", "Builder", "Step", "builder_config",
            "CbError", "CB_F32", "CB_BF16", "PAGE_SIZE", "LIB_PATH", "load"]
 
 
@@ -119,6 +119,36 @@ def attention_step(q, k_cache, v_cache, block_tables, query_start_loc, context_l
         _dev(q_offsets, "q_offsets", torch.int32), B, num_decodes, T, max_context_len, hq, hkv, d,
         PAGE_SIZE, P, float(scale), int(sliding_window), dt, _dev(out, "out"), ws_ptr, ws_bytes,
         _stream(stream)))
+    return out
+
+
+def attention_step_noalloc(q, k_cache, v_cache, block_tables, query_start_loc, context_lens, q_offsets,
+                           num_decodes: int, max_context_len: int, scale: float, out=None, stream=None,
+                           sliding_window: int = 0):
+    """``attention_step`` through cb_attention_step_noalloc: no workspace; the
+    library's fixed per-device scratch array is used instead (``out`` is still
+    allocated here when not given)."""
+    torch = _torch()
+    T, hq, d = q.shape
+    P, hkv = k_cache.shape[0], k_cache.shape[1]
+    B = context_lens.numel()
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs, stride]")
+    if query_start_loc.numel() != B + 1 or q_offsets.numel() != B:
+        raise ValueError("query_start_loc must be [B+1] and q_offsets [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    check(load().cb_attention_step_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+        _dev(q_offsets, "q_offsets", torch.int32), B, num_decodes, T, max_context_len, hq, hkv, d,
+        PAGE_SIZE, P, float(scale), int(sliding_window), dt, _dev(out, "out"), _stream(stream)))
     return out
 
 

@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libcb.so")
 PROBE = os.path.join(PKG, "hbm_probe")   # streaming-bandwidth probe (measurement aid)
 
 ARCH = "gfx950"
-SOURCES = ["cb_api.cpp", "builder.cpp", "engine.cpp", "kv_append.hip", "attn_f32.hip", "attn_bf16.hip"]
+SOURCES = ["cb_api.cpp", "builder.cpp", "engine.cpp", "kv_append.hip", "attn_f32.hip", "attn_bf16.hip",
+           "noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -190,6 +190,36 @@ int cb_attention_step(const void* q, const void* k_cache, const void* v_cache,
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * cb_attention_step_noalloc -- cb_attention_step for callers that cannot
+ * allocate device memory (work recorded under graph capture, tight serving
+ * loops, harnesses that forbid allocation).
+ *
+ * Same arguments, semantics, errors and kernels as cb_attention_step, without
+ * the workspace: the bf16 path's work lists and split-K partial results live
+ * in a fixed device array of CB_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends.  Nothing is allocated
+ * or freed by the call.  A step whose cb_attention_workspace_bytes exceeds
+ * the array is refused with CB_ERR_WORKSPACE before any device work.  The
+ * array's contents on entry do not matter (every list and partial a step
+ * reads is written by that step first); all calls on one device share it, so
+ * calls ordered on one stream are safe and calls that overlap on one device
+ * (unordered streams) race.  The f32 path needs no scratch.
+ * ------------------------------------------------------------------------- */
+#define CB_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+int cb_attention_step_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              const int32_t* q_offsets, int32_t num_seqs, int32_t num_decodes,
+                              int32_t num_tokens, int32_t max_context_len, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, float scale, int32_t sliding_window, int32_t dtype,
+                              void* out, void* stream);
+
+/* Size of that array in bytes (CB_NOALLOC_SCRATCH_BYTES). */
+size_t cb_attention_noalloc_scratch_bytes(void);
+
+/* ----------------------------------------------------------------------------
  * cb_profile_events -- timing hook for the main attention kernel.
  *
  * Not on the pages; a measurement aid.  start_event / stop_event are
