@@ -115,6 +115,8 @@ def main():
                     help="write a 1 GiB scratch buffer before every timed step so that no cache level holds "
                          "the step's data (auto: on when the step moves less than 1 GB); the step time is then "
                          "the device span of each step")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock measurement of MFMA-bound steps (40 extra back-to-back calls)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
     args = ap.parse_args()
@@ -257,9 +259,21 @@ def main():
     roof["span_us_p10_p50_p90"] = [pct(span_ms, 10), pct(span_ms, 50), pct(span_ms, 90)]
     roof["timing"] = ("cold: 1 GiB written before each step; step = device span" if cold
                       else "warm: steps back to back; step = wall time")
-    if roof["bound"] == "mfma":  # the shader clock the chip holds under this load
-        clk = gpu_clock_during(lambda: one_step(flush=False), 1.5)
-        torch.cuda.synchronize()
+    if roof["bound"] == "mfma" and not args.no_clock:  # the shader clock the chip holds under this load
+        # the step's attention called back to back on its own descriptor (the
+        # host enqueues far faster than the kernel runs, so the chip stays busy)
+        dq = [torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev) for a in
+              (desc0.block_tables, desc0.query_start_loc, desc0.context_lens, desc0.q_offsets)]
+        ws = torch.empty(max(cb.attention_workspace_bytes(desc0.num_seqs, desc0.num_decodes, T, hq, hkv, d,
+                                                          desc0.max_context_len, cb.CB_BF16), 1),
+                         dtype=torch.uint8, device=dev)
+        o2 = torch.empty_like(q[:T])
+
+        def attention_burst():
+            for _ in range(8):
+                cb.attention_step(q[:T], layer.k_cache, layer.v_cache, *dq, desc0.num_decodes, desc0.max_context_len,
+                                  layer.scale, out=o2, workspace=ws, stream=stream)
+        clk = kernel_clock_mhz(attention_burst, lib, dev)
         roof["clock_mhz"] = clk
         if clk and clk.get("mean"):
             # the same rate against the MFMA peak scaled to the measured clock (the published peak assumes 2.4 GHz)
@@ -398,59 +412,31 @@ def run_trace(args, dev):
     print(json.dumps(rec), flush=True)
 
 
-def gpu_clock_during(step_fn, seconds):
-    """Shader clock (MHz) the driver reports while ``step_fn`` runs back to back
-    for about ``seconds``: amdsmi GPU metrics sampled every 5 ms from a thread
-    (the per-XCD current clocks averaged).  None when the metrics are not
-    readable here."""
-    import threading
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
-    except Exception:
-        return None
-
-    def read():
-        m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
-            v = m.get(key)
-            vals = v if isinstance(v, list) else [v]
-            vals = [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
-            if vals:
-                return sum(vals) / len(vals), key
-        return None
-
-    samples, key, stop = [], [], threading.Event()
-
-    def loop():
-        while not stop.is_set():
-            try:
-                r = read()
-                if r:
-                    samples.append(r[0])
-                    key[:] = [r[1]]
-            except Exception:
-                pass
-            stop.wait(0.005)
-
-    th = threading.Thread(target=loop, daemon=True)
-    th.start()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        step_fn()
-    stop.set()
-    th.join()
-    try:
-        amdsmi.amdsmi_shut_down()
-    except Exception:
-        pass
-    if not samples:
-        return None
+def kernel_clock_mhz(burst, lib, dev, n=5):
+    """Shader clock (MHz) of the main attention kernel while it runs back to
+    back: the library's clock hook (cb_profile_clock) has workgroup 0 record
+    the shader-clock counter and the 100 MHz real-time counter at its start
+    and end; ``burst()`` enqueues several calls, and the last call's record of
+    each of ``n`` bursts is read."""
     import numpy as np
-    return {"mean": round(float(np.mean(samples)), 1), "p10": round(float(np.percentile(samples, 10)), 1),
-            "p90": round(float(np.percentile(samples, 90)), 1), "samples": len(samples),
-            "source": f"amdsmi gpu_metrics {key[0] if key else '?'}, back-to-back steps for {seconds} s"}
+    import torch
+    buf = torch.zeros(4, dtype=torch.int64, device=dev)
+    vals = []
+    lib.cb_profile_clock(buf.data_ptr())
+    try:
+        for _ in range(n):
+            burst()
+            torch.cuda.synchronize()
+            c0, t0, c1, t1 = (int(x) for x in buf.cpu().tolist())
+            if t1 > t0 and c1 > c0:
+                vals.append((c1 - c0) * 100.0 / (t1 - t0))
+    finally:
+        lib.cb_profile_clock(None)
+    if not vals:
+        return None
+    return {"mean": round(float(np.mean(vals)), 1), "min": round(float(np.min(vals)), 1),
+            "max": round(float(np.max(vals)), 1), "samples": len(vals),
+            "source": "s_memtime over s_memrealtime across workgroup 0 of the last of 8 back-to-back calls"}
 
 
 def achievable_read_gbs(nbytes):

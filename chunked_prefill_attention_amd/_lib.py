@@ -63,6 +63,7 @@ SIGNATURES = {
     "cb_last_error": (C.c_char_p, []),
     "cb_abi_version": (C.c_int, []),
     "cb_profile_events": (C.c_int, [vp, vp]),
+    "cb_profile_clock": (C.c_int, [vp]),
     "cb_attention_step_noalloc": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                             i32, i32, f32, i32, i32, vp, vp]),
     "cb_attention_noalloc_scratch_bytes": (sz, []),

@@ -158,7 +158,18 @@ struct Params {
   int32_t comb_dec_blocks;
   int32_t window;        // sliding window in tokens; 0 = none
   float scale_log2;      // softmax scale * log2(e)
+  // measurement hook: when set, workgroup 0 writes its (shader-clock counter,
+  // 100 MHz real-time counter) at start and end here (4 values)
+  unsigned long long* clk;
 };
+
+// Workgroup 0's clock record (measurement hook, off unless p.clk is set).
+__device__ __forceinline__ void clock_mark(const Params& p, int at) {
+  if (p.clk && blockIdx.x == 0 && threadIdx.x == 0) {
+    p.clk[2 * at] = __builtin_amdgcn_s_memtime();
+    p.clk[2 * at + 1] = __builtin_amdgcn_s_memrealtime();
+  }
+}
 
 template <int D>
 struct PfLds {
@@ -813,8 +824,9 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
   const int kfloor = window_first_key(off + tile * PF_ROWS / G, W);  // no row of the tile sees below
   const int w_first_row = tile * PF_ROWS + wv * 32;
   const int w_last_row = min(w_first_row + 31, R - 1);
-  const int w_kend = (w_first_row < R) ? min(ctx, off + w_last_row / G + 1) : 0;
-  const int w_kfull = min(ctx, off + w_first_row / G + 1);  // keys below are visible to every row...
+  const int w_kend = __builtin_amdgcn_readfirstlane((w_first_row < R) ? min(ctx, off + w_last_row / G + 1) : 0);
+  // keys below are visible to every row...
+  const int w_kfull = __builtin_amdgcn_readfirstlane(min(ctx, off + w_first_row / G + 1));
   const int w_klo_min = window_first_key(off + w_first_row / G, W);  // ...and at or above the window
   const int w_klo_max = window_first_key(off + w_last_row / G, W);  // of the wave's last row
 
@@ -1041,16 +1053,21 @@ __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kerne
   } else {
     return;  // past the live work (the grid is sized by the caps): nothing to do
   }
+  clock_mark(p, 0);
   if (pf >= 0) {
     prefill_tile<D, WIN>(p, pf);
+    clock_mark(p, 1);
     return;
   }
   decode_wave<D, WIN, (WIN ? CB_NT_MIXED_WINDOW : CB_NT_MIXED) != 0>(p, dec * PF_WAVES + (threadIdx.x >> 6));
+  clock_mark(p, 1);
 }
 
 template <int D, bool WIN>
 __global__ __launch_bounds__(CB_DEC_WG, CB_DEC_WAVES_PER_SIMD) void attn_decode_kernel(Params p) {
+  clock_mark(p, 0);
   decode_wave<D, WIN, CB_NT_DECODE>(p, (int)blockIdx.x * (CB_DEC_WG / 64) + (threadIdx.x >> 6));
+  clock_mark(p, 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1207,6 +1224,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.pf_tile_cap = (int32_t)pl.pf_tile_cap;
   p.pf_item_cap = (int32_t)pl.pf_item_cap;
   p.scale_log2 = a.scale * LOG2E;
+  p.clk = static_cast<unsigned long long*>(g_prof_clock);
   p.window = a.window;
   const int64_t pf_blocks = pl.pf_item_cap * a.hkv;
   const int64_t dec_blocks = (pl.dec_cap * a.hkv + PF_WAVES - 1) / PF_WAVES;

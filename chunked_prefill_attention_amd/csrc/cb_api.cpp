@@ -18,6 +18,7 @@ thread_local char g_err[512] = "";
 
 thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
+thread_local void* g_prof_clock = nullptr;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -77,6 +78,12 @@ int cb_profile_events(void* start_event, void* stop_event) {
     return cb::fail(CB_ERR_INVALID, "cb_profile_events: pass two events or none");
   cb::g_prof_start = static_cast<hipEvent_t>(start_event);
   cb::g_prof_stop = static_cast<hipEvent_t>(stop_event);
+  return CB_OK;
+}
+
+int cb_profile_clock(void* device_buffer) {
+  cb::clear_error();
+  cb::g_prof_clock = device_buffer;
   return CB_OK;
 }
 

@@ -14,11 +14,14 @@ namespace cb {
 // null when profiling is off.  Per host thread.
 extern thread_local hipEvent_t g_prof_start;
 extern thread_local hipEvent_t g_prof_stop;
+// Device buffer of 4 uint64 for the main kernel's clock record (null: off).
+extern thread_local void* g_prof_clock;
 // Suspends the profiling events of this thread for a scope (graph capture).
 struct ProfileEventsOff {
   hipEvent_t start = g_prof_start, stop = g_prof_stop;
-  ProfileEventsOff() { g_prof_start = g_prof_stop = nullptr; }
-  ~ProfileEventsOff() { g_prof_start = start; g_prof_stop = stop; }
+  void* clock = g_prof_clock;
+  ProfileEventsOff() { g_prof_start = g_prof_stop = nullptr; g_prof_clock = nullptr; }
+  ~ProfileEventsOff() { g_prof_start = start; g_prof_stop = stop; g_prof_clock = clock; }
 };
 
 // Arguments of one attention step, already validated on the host.

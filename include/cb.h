@@ -234,6 +234,20 @@ size_t cb_attention_noalloc_scratch_bytes(void);
 int cb_profile_events(void* start_event, void* stop_event);
 
 /* ----------------------------------------------------------------------------
+ * cb_profile_clock -- clock record of the main attention kernel.
+ *
+ * Not on the pages; a measurement aid.  device_buffer is caller-owned device
+ * memory of 4 uint64 (or NULL to turn the hook off).  Subsequent
+ * cb_attention_step calls made by the calling thread have workgroup 0 of the
+ * main bf16 attention kernel write, at its start and at its end, the shader
+ * clock counter (s_memtime) and the 100 MHz real-time counter
+ * (s_memrealtime): {cycles0, ticks0, cycles1, ticks1}.  The shader clock in
+ * MHz over that workgroup's life is (cycles1 - cycles0) * 100 / (ticks1 -
+ * ticks0).  Host bookkeeping only; returns CB_OK.
+ * ------------------------------------------------------------------------- */
+int cb_profile_clock(void* device_buffer);
+
+/* ----------------------------------------------------------------------------
  * FIFO batch builder (host only; touches no device).
  *
  * [CBA] "Scheduler": three limits per forward pass -- the token budget
