@@ -95,7 +95,9 @@ int cb_engine_create(const cb_engine_config* config, cb_engine** out) {
   int st = cb_builder_create(&c.builder, &e->builder);
   if (st != CB_OK) { delete e; return st; }
   for (int i = 0; i < 2; ++i) {
-    if (hipEventCreateWithFlags(&e->copied[i], hipEventDisableTiming) != hipSuccess) {
+    // the host only needs to know that the slot's reader finished: no
+    // system-scope writeback of device memory when the event is recorded
+    if (hipEventCreateWithFlags(&e->copied[i], hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
       cb_engine_destroy(e);
       return cb::fail(CB_ERR_DEVICE, "cb_engine_create: hipEventCreate failed");
     }
