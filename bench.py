@@ -119,12 +119,11 @@ def counted_traffic(workload_name, kernel):
     return None
 
 
-def sub_desc(desc, sel):
-    """The sequences ``sel`` (a slice) of a step descriptor, for algorithmic()."""
-    import types
-    ql = desc.q_lens[sel]
-    return types.SimpleNamespace(context_lens=desc.context_lens[sel], q_lens=ql, num_tokens=int(ql.sum()),
-                                 num_seqs=len(ql))
+def first_held_position(builder, req_id):
+    """First logical position of a request whose page the builder holds."""
+    import numpy as np
+    held = np.nonzero(np.asarray(builder.block_table(req_id)) >= 0)[0]
+    return int(held[0]) * 16 if len(held) else 1 << 30
 
 
 def algorithmic(desc, hq, hkv, d, esize, window=0):
@@ -208,8 +207,11 @@ def main():
         k = wl.device_normal((n, hkv, d), w.dtype, dev, w.seed, i, 1)
         v = wl.device_normal((n, hkv, d), w.dtype, dev, w.seed, i, 2)
         hist[i] = (k, v)
-        if c > 0:
-            layer.write_positions(i, 0, c, k[:c], v[:c])
+        # the cached history the builder holds pages for (under a sliding
+        # window, pages wholly below the next row's window are not held)
+        lo = min(first_held_position(layer.builder, i), c)
+        if lo < c:
+            layer.write_positions(i, lo, c, k[lo:c], v[lo:c])
     for _ in range(advance):                       # earlier steps: append only
         desc = layer.schedule()
         ks = torch.cat([hist[int(r)][0][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
@@ -224,9 +226,6 @@ def main():
     out = torch.empty_like(q)
     layer.attend(q, kn, vn, out=out)               # sizes the workspace
     torch.cuda.synchronize()
-    # a step whose prefill part is small (or large) beside its decode part runs
-    # as two launches: the prefill items, then the decode-only kernel
-    two_launch = layer.stats()["two_launch_steps"] > 0
     if layer.graphs:                               # the step's inputs live in the static buffers
         layer.static_q[:T].copy_(q)
         layer.static_k[:T].copy_(kn)
@@ -245,12 +244,11 @@ def main():
     stops = [TimingEvent() for _ in range(args.steps)]
     span0 = [TimingEvent() for _ in range(args.steps)]
     span1 = [TimingEvent() for _ in range(args.steps)]
-    mids = [TimingEvent() for _ in range(args.steps)] if two_launch else []
-    for e in starts + stops + span0 + span1 + mids:
+    for e in starts + stops + span0 + span1:
         e.record()
     stream = layer.graph_stream if layer.graphs else torch.cuda.current_stream(dev)
 
-    def one_step(k=None, flush=True, span=None, part=None):
+    def one_step(k=None, flush=True, span=None):
         if cold and flush:                                     # evict the step's data from L2 and MALL
             with torch.cuda.stream(stream):
                 scratch.fill_(k or 0)
@@ -267,17 +265,11 @@ def main():
             lib.cb_profile_events(starts[k].cuda_event, stops[k].cuda_event)
         elif span is not None:  # the span pass: events around the whole step
             span0[span].record(stream)
-        elif part is not None:  # the parts pass: start, mid and stop around the two launches
-            lib.cb_profile_events(span0[part].cuda_event, span1[part].cuda_event)
-            lib.cb_profile_split_event(mids[part].cuda_event)
         layer.attend(q, kn, vn, out=out, stream=stream)        # a3 .. a7
         if k is not None:
             lib.cb_profile_events(None, None)
         elif span is not None:
             span1[span].record(stream)
-        elif part is not None:
-            lib.cb_profile_events(None, None)
-            lib.cb_profile_split_event(None)
 
     for i in range(args.warmup):
         one_step()
@@ -299,66 +291,30 @@ def main():
         torch.cuda.synchronize()
         span_ms = [s.elapsed_time(e) for s, e in zip(span0, span1)]
     span_s = float(np.mean(span_ms)) / 1e3
-    part_ms = None
-    if two_launch and not layer.graphs:   # a third pass: each of the two launches timed on its own
-        for k in range(args.steps):
-            one_step(part=k)
-        torch.cuda.synchronize()
-        part_ms = ([s.elapsed_time(m) for s, m in zip(span0, mids)], [m.elapsed_time(e) for m, e in zip(mids, span1)])
     if cold:              # the wall clock includes the flushes: a step is its device span
         step_s = span_s
     assert torch.isfinite(out[:T].float()).all(), "non-finite attention output"
 
     t_hbm, t_mfma = bytes_alg / (HBM_PEAK_GBS * 1e9), flops_alg / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-    tmpl = f"<{d}, {'true' if args.window > 0 else 'false'}>"
-    kname = "attn_mixed_kernel" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel"
-    launches = None
-    if part_ms is not None:
-        # two launches: the roofline is the longer one's, on its own part of
-        # the step; both are listed, and the pair's figure beside them
-        nd = desc0.num_decodes
-        parts = {"prefill": sub_desc(desc0, slice(nd, desc0.num_seqs)), "decode": sub_desc(desc0, slice(0, nd))}
-        launches = []
-        for (name, sd), ms in zip(parts.items(), part_ms):
-            b_, f_ = algorithmic(sd, hq, hkv, d, esize, args.window)[:2]
-            s_ = float(np.mean(ms)) / 1e3
-            bound = "hbm" if b_ / (HBM_PEAK_GBS * 1e9) >= f_ / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
-            launches.append({"kernel": ("attn_mixed_kernel" if name == "prefill" else "attn_decode_kernel") + tmpl,
-                             "items": name, "us": round(s_ * 1e6, 2), "algorithmic_bytes": b_,
-                             "algorithmic_flops": f_, "bound": bound,
-                             "frac": round((b_ / s_ / 1e9 / HBM_PEAK_GBS) if bound == "hbm"
-                                           else (f_ / s_ / 1e12 / MFMA_BF16_PEAK_TFLOPS), 4)})
-        dom = max(launches, key=lambda x: x["us"])
-        dom_ms = part_ms[launches.index(dom)]
-        kname, b_dom, f_dom, s_dom = dom["kernel"][:-len(tmpl)], dom["algorithmic_bytes"], dom["algorithmic_flops"], dom["us"] / 1e6
-        hbm_dom = dom["bound"] == "hbm"
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(bytes_alg / kern_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(bytes_alg / kern_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
     else:
-        b_dom, f_dom, s_dom, hbm_dom = bytes_alg, flops_alg, kern_s, t_hbm >= t_mfma
-        dom_ms = kern_ms
-    if hbm_dom:
-        roof = {"bound": "hbm", "achieved": round(b_dom / s_dom / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(b_dom / s_dom / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        roof = {"bound": "mfma", "achieved": round(f_dom / s_dom / 1e12, 1),
+        roof = {"bound": "mfma", "achieved": round(flops_alg / kern_s / 1e12, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(f_dom / s_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = kname + tmpl   # the template instance timed
+                "frac": round(flops_alg / kern_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+    kname = "attn_mixed_kernel" if desc0.num_seqs > desc0.num_decodes else "attn_decode_kernel"
+    roof["kernel"] = f"{kname}<{d}, {'true' if args.window > 0 else 'false'}>"   # the template instance timed
     roof["traffic"] = counted_traffic(w.name, roof["kernel"])
-    if launches is not None:
-        roof["launches"] = launches
-        roof["kernel_algorithmic_bytes"] = b_dom
-        # both launches (and the gap between them) against the step's whole work
-        roof["attention_us"] = round(kern_s * 1e6, 2)
-        roof["attention_frac"] = round(max(t_hbm, t_mfma) / kern_s, 4)
     if layer.graphs:
         roof["kernel"] = "graph replay (kv_append + attention + combine)"
         roof["traffic"] = None
         roof["graphs"] = layer.graph_stats()
-    roof["kernel_us"] = round(s_dom * 1e6, 2)
+    roof["kernel_us"] = round(kern_s * 1e6, 2)
     roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
     roof["device_span_us"] = round(span_s * 1e6, 2)   # kv_append .. combine on the device
     pct = lambda xs, q: round(float(np.percentile(xs, q)) * 1e3, 2)
-    roof["kernel_us_p10_p50_p90"] = [pct(dom_ms, 10), pct(dom_ms, 50), pct(dom_ms, 90)]
+    roof["kernel_us_p10_p50_p90"] = [pct(kern_ms, 10), pct(kern_ms, 50), pct(kern_ms, 90)]
     roof["span_us_p10_p50_p90"] = [pct(span_ms, 10), pct(span_ms, 50), pct(span_ms, 90)]
     roof["timing"] = ("cold: 1 GiB written before each step; step = device span" if cold
                       else "warm: steps back to back; step = wall time; HIP events around the main kernel only "

@@ -54,8 +54,7 @@ class EngineConfig(C.Structure):
 
 class EngineStats(C.Structure):
     _fields_ = [("steps_scheduled", i64), ("steps_attended", i64), ("slot_waits", i64),
-                ("graph_captures", i64), ("graph_replays", i64), ("graphs_cached", i64),
-                ("two_launch_steps", i64)]
+                ("graph_captures", i64), ("graph_replays", i64), ("graphs_cached", i64)]
 
 
 # name -> (restype, argtypes); one line per declaration of include/cb.h
@@ -65,7 +64,6 @@ SIGNATURES = {
     "cb_abi_version": (C.c_int, []),
     "cb_profile_events": (C.c_int, [vp, vp]),
     "cb_profile_clock": (C.c_int, [vp]),
-    "cb_profile_split_event": (C.c_int, [vp]),
     "cb_attention_step_noalloc": (C.c_int, [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                             i32, i32, f32, i32, i32, vp, vp]),
     "cb_attention_noalloc_scratch_bytes": (sz, []),

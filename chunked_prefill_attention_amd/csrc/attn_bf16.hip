@@ -343,36 +343,6 @@ __host__ __device__ inline int mix_order(int64_t pf_live_items, int64_t dec_live
   return (pf_live_items * hkv > slots && dec_live_items > 0) ? 1 : 0;
 }
 
-// One launch or two.  Sharing a launch lets a long prefill chunk's MFMA work
-// run beside the decodes' HBM streaming, but every block of the ragged
-// launch carries the prefill path's registers and LDS, and a decode
-// workgroup that shares a CU with a prefill workgroup slows down.  When the
-// prefill part is small beside the decode part there is little to overlap,
-// so the host list builder then runs the prefill items in a launch of their
-// own and the decode items in the decode-only kernel (its occupancy and
-// non-temporal loads).  The estimate compares the prefill part's MFMA work
-// at ~0.95 PFLOP/s with the decode part's K/V bytes at ~6 TB/s (both as this
-// kernel reaches them on MI355X); head size and KV heads cancel out.
-#ifndef CB_SPLIT_RULE       // 0: one launch; 1: two launches whenever both kinds are live; 2: by the estimate
-#define CB_SPLIT_RULE 2
-#endif
-#ifndef CB_SPLIT_RATIO      // two launches when prefill time < this share of decode time ...
-#define CB_SPLIT_RATIO 0.5
-#endif
-#ifndef CB_SPLIT_RATIO_HI   // ... or above this multiple of it (0: never)
-#define CB_SPLIT_RATIO_HI 2.0
-#endif
-#ifndef CB_PF_SPLIT_MIN_KEYS  // two launches: shortest prefill key range per item (a multiple of 64)
-#define CB_PF_SPLIT_MIN_KEYS 384
-#endif
-inline bool split_launch(double pf_pairs, double dec_pages, int G) {
-  if (CB_SPLIT_RULE == 0 || pf_pairs <= 0 || dec_pages <= 0) return false;
-  if (CB_SPLIT_RULE == 1) return true;
-  const double t_pf = pf_pairs * 4.0 * G / 0.95e15;   // flops per (row, key) pair and head dim, per query head of a KV head
-  const double t_dec = dec_pages * 64.0 / 6.0e12;      // K + V bytes per page and head dim, per KV head
-  return t_pf < CB_SPLIT_RATIO * t_dec || (CB_SPLIT_RATIO_HI > 0 && t_pf > CB_SPLIT_RATIO_HI * t_dec);
-}
-
 __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   __shared__ int sh[40];
   const int tid = threadIdx.x;
@@ -1261,7 +1231,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.pf_blocks = (int32_t)pf_blocks;
   p.dec_blocks = (int32_t)dec_blocks;
   p.slots = pl.slots > 0 ? pl.slots : mixed_slots(D);
-  const bool dec_splits = pl.dec_may_split;
+  const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
   const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
   const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv * (PF_ROWS / CP_ROWS) : 0;
   p.comb_dec_blocks = (int32_t)comb_dec;
@@ -1278,23 +1248,9 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   }
   if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
   const bool win = a.window > 0;
-  const bool live = lists && lists->live_pf_items >= 0 && lists->live_dec_items >= 0;
-  if (pf_blocks > 0 && live && lists->split && lists->live_pf_items > 0 && lists->live_dec_items > 0) {
-    // two launches: the prefill items alone (no decode blocks in this grid),
-    // then the decode items in the decode-only kernel
-    Params pp = p;
-    pp.dec_blocks = 0;
-    const dim3 pgrid((unsigned)std::min<int64_t>(pf_blocks, lists->live_pf_items * a.hkv));
-    if (win) hipLaunchKernelGGL((attn_mixed_kernel<D, true>), pgrid, dim3(PF_THREADS), 0, stream, pp);
-    else hipLaunchKernelGGL((attn_mixed_kernel<D, false>), pgrid, dim3(PF_THREADS), 0, stream, pp);
-    if (g_prof_mid) (void)hipEventRecord(g_prof_mid, stream);
-    const int64_t waves = std::min<int64_t>(pl.dec_cap, lists->live_dec_items) * a.hkv;
-    const dim3 dgrid((unsigned)((waves + CB_DEC_WG / 64 - 1) / (CB_DEC_WG / 64)));
-    if (win) hipLaunchKernelGGL((attn_decode_kernel<D, true>), dgrid, dim3(CB_DEC_WG), 0, stream, p);
-    else hipLaunchKernelGGL((attn_decode_kernel<D, false>), dgrid, dim3(CB_DEC_WG), 0, stream, p);
-  } else if (pf_blocks > 0) {
+  if (pf_blocks > 0) {
     int64_t nblk = pf_blocks + dec_blocks;
-    if (live)
+    if (lists && lists->live_pf_items >= 0 && lists->live_dec_items >= 0)
       nblk = std::min<int64_t>(pf_blocks, lists->live_pf_items * a.hkv) +
              std::min<int64_t>(dec_blocks, (lists->live_dec_items * a.hkv + PF_WAVES - 1) / PF_WAVES);
     const dim3 grid((unsigned)std::max<int64_t>(nblk, 1));
@@ -1335,18 +1291,24 @@ int mixed_slots(int head_dim) {
   return v;
 }
 
-namespace {
-
-// The decode split (pages per wavefront): the longest of {max_split, ..., 16}
-// that gives the decode grid >= min_waves wavefronts for sequences of
-// max_pages pages, else 8; then, under a sliding window, the longest split
-// that keeps the same item budget per sequence.  Sets split_pages and dec_cap.
-void plan_decode(Bf16Plan& pl, int32_t num_decodes, int32_t hkv, int64_t max_pages, int32_t window,
-                 int64_t min_waves, int max_split) {
+Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq, int32_t hkv,
+                   int32_t head_dim, int32_t max_context_len, int32_t window) {
+  Bf16Plan pl{};
+  const int64_t max_pages = (max_context_len + 15) / 16;
+  const int64_t G = hkv > 0 ? hq / hkv : 1;
+  // decode: the longest split (pages per wavefront) that still gives the
+  // decode grid >= 8k wavefronts (about 2-3 rounds of the chip's wave slots),
+  // or >= 4k when no prefill work shares the launch; longer splits write
+  // fewer partials for the combine and start fewer wavefronts.  max_pages is
+  // the step's longest context, which in a mixed step is usually a prefill
+  // sequence's, so there the wave count is overestimated: mixed launches
+  // stop at 64-page splits.
   const int64_t lanes = (int64_t)num_decodes * hkv;
+  const bool with_prefill = num_seqs > num_decodes;
+  const int64_t min_waves = with_prefill ? CB_DEC_MIN_WAVES : CB_DEC_MIN_WAVES_ALONE;
   pl.split_pages = 8;
   for (int sp : {DEC_MAX_SPLIT, 64, 32, 16}) {
-    if (sp > max_split) continue;
+    if (with_prefill && sp > 64) continue;
     if (lanes * ((max_pages + sp - 1) / sp) >= min_waves) { pl.split_pages = sp; break; }
   }
   // the items per decode sequence this allows sizes the work lists and the
@@ -1360,7 +1322,7 @@ void plan_decode(Bf16Plan& pl, int32_t num_decodes, int32_t hkv, int64_t max_pag
     const int64_t wpages = std::min<int64_t>(max_pages, ((int64_t)window + 15) / 16 + 1);
     int best = pl.split_pages;
     for (int sp : {DEC_MAX_SPLIT, 64, 32, 16, 8}) {
-      if (sp > max_split) continue;
+      if (with_prefill && sp > 64) continue;
       const int64_t items = (wpages + sp - 1) / sp;
       if (items > budget) break;  // shorter splits need even more items
       best = sp;
@@ -1368,17 +1330,16 @@ void plan_decode(Bf16Plan& pl, int32_t num_decodes, int32_t hkv, int64_t max_pag
     }
     pl.split_pages = best;
   }
-  pl.dec_may_split = num_decodes > 0 && (int64_t)pl.split_pages < max_pages;
-}
-
-// Prefill items: row tiles bound by the query tokens, key ranges of ks keys;
-// a tile sees at most max_keys keys.  Then the workspace layout.
-void plan_prefill_and_layout(Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hkv,
-                             int64_t G, int32_t head_dim, int64_t ks, int64_t max_keys) {
+  // prefill: row tiles bound by the query tokens; key ranges cut so that about
+  // 1024 workgroups exist when the tiles are long, never below 512 keys
   const int64_t np = num_seqs - num_decodes;
   pl.pf_tile_cap = np > 0 ? ((int64_t)(num_tokens - num_decodes) * G + PF_ROWS - 1) / PF_ROWS + np : 0;
+  const int64_t tiles = pl.pf_tile_cap * hkv;
+  int64_t ks = tiles > 0 ? ((int64_t)max_context_len * tiles / CB_PF_TARGET_ITEMS + PF_KEYS - 1) / PF_KEYS * PF_KEYS
+                         : PF_KEYS;
+  ks = ks < CB_PF_MIN_KEYS ? CB_PF_MIN_KEYS : ks;
   pl.pf_split_keys = (int32_t)(ks > PF_MAX_KEYS ? PF_MAX_KEYS : ks);
-  const int64_t max_splits = (max_keys + pl.pf_split_keys - 1) / pl.pf_split_keys;
+  const int64_t max_splits = (max_context_len + pl.pf_split_keys - 1) / pl.pf_split_keys;
   pl.pf_item_cap = pl.pf_tile_cap * (max_splits > 0 ? max_splits : 1);
   pl.pf_may_split = max_splits > 1;
   pl.hkv = hkv;
@@ -1397,73 +1358,6 @@ void plan_prefill_and_layout(Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes
   pl.off_pf_ml = off;       off = align(off + prows * 8);
   pl.off_pf_o = off;        off = align(off + prows * head_dim * sizeof(float));
   pl.bytes = off;
-}
-
-}  // namespace
-
-Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq, int32_t hkv,
-                   int32_t head_dim, int32_t max_context_len, int32_t window) {
-  Bf16Plan pl{};
-  const int64_t max_pages = (max_context_len + 15) / 16;
-  const int64_t G = hkv > 0 ? hq / hkv : 1;
-  // decode: the longest split that still gives the decode grid >= 8k
-  // wavefronts (about 2-3 rounds of the chip's wave slots), or >= 4k when no
-  // prefill work shares the launch; longer splits write fewer partials for
-  // the combine and start fewer wavefronts.  max_pages is the step's longest
-  // context, which in a mixed step is usually a prefill sequence's, so there
-  // the wave count is overestimated: mixed launches stop at 64-page splits.
-  const bool with_prefill = num_seqs > num_decodes;
-  plan_decode(pl, num_decodes, hkv, max_pages, window, with_prefill ? CB_DEC_MIN_WAVES : CB_DEC_MIN_WAVES_ALONE,
-              with_prefill ? 64 : DEC_MAX_SPLIT);
-  // prefill: key ranges cut so that about 1024 workgroups exist when the
-  // tiles are long, never below 512 keys
-  const int64_t np = num_seqs - num_decodes;
-  const int64_t tiles = (np > 0 ? ((int64_t)(num_tokens - num_decodes) * G + PF_ROWS - 1) / PF_ROWS + np : 0) * hkv;
-  int64_t ks = tiles > 0 ? ((int64_t)max_context_len * tiles / CB_PF_TARGET_ITEMS + PF_KEYS - 1) / PF_KEYS * PF_KEYS
-                         : PF_KEYS;
-  ks = ks < CB_PF_MIN_KEYS ? CB_PF_MIN_KEYS : ks;
-  plan_prefill_and_layout(pl, num_seqs, num_decodes, num_tokens, hkv, G, head_dim, ks, max_context_len);
-  return pl;
-}
-
-StepShape step_shape(int32_t num_seqs, int32_t num_decodes, int32_t G, int32_t window, const int32_t* qsl,
-                     const int32_t* ctx, const int32_t* q_off) {
-  StepShape sh{};
-  for (int s = 0; s < num_decodes; ++s) {
-    sh.dec_pages += decode_pages(ctx[s], window);
-    sh.max_dec_ctx = std::max(sh.max_dec_ctx, ctx[s]);
-  }
-  for (int s = num_decodes; s < num_seqs; ++s) {
-    const int Lq = qsl[s + 1] - qsl[s];
-    if (Lq <= 0) continue;
-    sh.max_pf_ctx = std::max(sh.max_pf_ctx, ctx[s]);
-    for (int i = 0; i < Lq; ++i) {  // keys each query row sees
-      const int64_t pos = (int64_t)q_off[s] + i;
-      sh.pf_pairs += (double)(window > 0 ? std::min<int64_t>(pos + 1, window) : pos + 1);
-    }
-    const int ntiles = (Lq * G + PF_ROWS - 1) / PF_ROWS;
-    for (int t = 0; t < ntiles; ++t)
-      sh.pf_key_tiles += (tile_key_end(t, Lq, G, ctx[s], q_off[s]) - tile_key_base(t, G, q_off[s], window) +
-                          PF_KEYS - 1) / PF_KEYS;
-  }
-  sh.split = split_launch(sh.pf_pairs, sh.dec_pages, G);
-  return sh;
-}
-
-Bf16Plan plan_bf16_two_launches(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq, int32_t hkv,
-                                int32_t head_dim, int32_t window, const StepShape& sh, int32_t slots) {
-  Bf16Plan pl{};
-  const int64_t G = hkv > 0 ? hq / hkv : 1;
-  // the decodes alone in the decode-only kernel, sized by their own lengths
-  plan_decode(pl, num_decodes, hkv, ((int64_t)sh.max_dec_ctx + 15) / 16, window, CB_DEC_MIN_WAVES_ALONE,
-              DEC_MAX_SPLIT);
-  // the prefill alone: key ranges cut so that the heaviest item is about one
-  // slot's share of the prefill's key tiles (the launch finishes when its
-  // longest workgroup does), never below CB_PF_SPLIT_MIN_KEYS
-  const int64_t share = (sh.pf_key_tiles * hkv + std::max(slots, 1) - 1) / std::max(slots, 1);
-  int64_t ks = std::max<int64_t>(share, 1) * PF_KEYS;
-  ks = std::max<int64_t>(ks, CB_PF_SPLIT_MIN_KEYS);
-  plan_prefill_and_layout(pl, num_seqs, num_decodes, num_tokens, hkv, G, head_dim, ks, std::max(sh.max_pf_ctx, 1));
   return pl;
 }
 
@@ -1492,7 +1386,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
 // short last splits by decreasing length, sequences in order within a
 // length), prefill tiles heaviest (last) first with their key splits.
 WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G, int32_t window,
-                      const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst, bool split) {
+                      const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst) {
   const WorkListLayout L = work_list_layout(pl, num_decodes);
   uint8_t* base = static_cast<uint8_t*>(dst);
   int4* dec = reinterpret_cast<int4*>(base + L.dec_items);
@@ -1555,10 +1449,9 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
   for (int64_t i = nt; i < pl.pf_tile_cap; ++i) pft[i] = make_int4(-1, 0, 0, 0);
   for (int64_t i = ni; i < pl.pf_item_cap; ++i) pfi[i] = make_int4(-1, 0, 0, 0);
   const int64_t pl_live = std::min<int64_t>(ni, pl.pf_item_cap), dl_live = std::min<int64_t>(n, pl.dec_cap);
-  split = split && pl_live > 0 && dl_live > 0;
   *reinterpret_cast<int4*>(base + L.hdr) =
-      make_int4((int)pl_live, (int)dl_live, split ? 0 : mix_order(pl_live, dl_live, pl.hkv, pl.slots), 0);
-  return WorkCounts{pl_live, dl_live, split};
+      make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), 0);
+  return WorkCounts{pl_live, dl_live};
 }
 
 }  // namespace cb

@@ -18,7 +18,6 @@ thread_local char g_err[512] = "";
 
 thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
-thread_local hipEvent_t g_prof_mid = nullptr;
 thread_local void* g_prof_clock = nullptr;
 
 int fail(int status, const char* fmt, ...) {
@@ -71,7 +70,7 @@ const char* cb_status_string(int status) {
 
 const char* cb_last_error(void) { return cb::g_err; }
 
-int cb_abi_version(void) { return 4; }
+int cb_abi_version(void) { return 3; }
 
 int cb_profile_events(void* start_event, void* stop_event) {
   cb::clear_error();
@@ -79,12 +78,6 @@ int cb_profile_events(void* start_event, void* stop_event) {
     return cb::fail(CB_ERR_INVALID, "cb_profile_events: pass two events or none");
   cb::g_prof_start = static_cast<hipEvent_t>(start_event);
   cb::g_prof_stop = static_cast<hipEvent_t>(stop_event);
-  return CB_OK;
-}
-
-int cb_profile_split_event(void* mid_event) {
-  cb::clear_error();
-  cb::g_prof_mid = static_cast<hipEvent_t>(mid_event);
   return CB_OK;
 }
 
@@ -206,11 +199,8 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
       return cb::fail(CB_ERR_INVALID, "step too large for one launch");
     return device_status(cb::launch_attention_f32(a, st), "cb_attention_step launch (f32)");
   }
-  // the caller's lists may come with the plan they were built with
-  const cb::Bf16Plan plan = lists && lists->plan ? *lists->plan
-                                                 : cb::plan_bf16(num_seqs, num_decodes, num_tokens, num_q_heads,
-                                                                 num_kv_heads, head_dim, max_context_len,
-                                                                 sliding_window);
+  const cb::Bf16Plan plan = cb::plan_bf16(num_seqs, num_decodes, num_tokens, num_q_heads, num_kv_heads,
+                                          head_dim, max_context_len, sliding_window);
   if (plan.dec_cap * num_kv_heads >= (int64_t(1) << 31) || plan.pf_item_cap * num_kv_heads >= (int64_t(1) << 30) ||
       plan.pf_tile_cap * num_kv_heads >= (int64_t(1) << 27))   // the prefill combine runs 8 blocks per tile
     return cb::fail(CB_ERR_INVALID, "step too large for one launch");

@@ -53,7 +53,6 @@ struct cb_engine {
   const int32_t* h_slots_dev = nullptr;  // the slot mapping in the staging slot, device address
   bool have_lists = false;  // bf16: the step's work lists were built on the host
   cb::WorkLists lists{};
-  cb::Bf16Plan plan{};      // the plan they were built with (lists.plan points here when it is not plan_bf16's)
   // the pending step as launched: the builder's sizes, or their padded shape
   int32_t x_nseq = 0, x_ndec = 0, x_ntok = 0, x_maxctx = 0, x_stride = 0;
   // graph replay
@@ -63,7 +62,6 @@ struct cb_engine {
   int64_t n_captures = 0, n_replays = 0;
   int64_t n_scheduled = 0, n_attended = 0;
   int64_t n_slot_waits = 0;  // schedules whose staging slot was still being read, and waited
-  int64_t n_two_launch = 0;  // attended steps that ran as two launches
   void drop_graphs() {
     for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
@@ -242,29 +240,17 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     for (int32_t t = d.num_tokens; t < e->x_ntok; ++t) h[off++] = -1;
   }
   e->have_lists = false;
-  e->lists.plan = nullptr;
-  e->lists.split = false;
   if (e->cfg.dtype == CB_BF16 && e->x_ntok > 0) {
-    // the attention step's work lists, built here instead of by a device plan
-    // kernel; outside graph capture the step's contents may choose two launches
-    const int32_t G = e->cfg.num_q_heads / e->cfg.num_kv_heads;
-    const int32_t win = e->cfg.builder.sliding_window;
-    const int32_t slots = cb::mixed_slots(e->cfg.head_dim);  // the lists' block order depends on it
-    cb::StepShape shape{};
-    if (!e->capture) shape = cb::step_shape(e->x_nseq, e->x_ndec, G, win, h + o_qsl, h + o_ctx, h + o_off);
-    cb::Bf16Plan pl = shape.split
-        ? cb::plan_bf16_two_launches(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads, e->cfg.num_kv_heads,
-                                     e->cfg.head_dim, win, shape, slots)
-        : cb::plan_bf16(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads, e->cfg.num_kv_heads,
-                        e->cfg.head_dim, std::max(e->x_maxctx, 1), win);
-    pl.slots = slots;
+    // the attention step's work lists, built here instead of by a device plan kernel
+    cb::Bf16Plan pl = cb::plan_bf16(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads,
+                                    e->cfg.num_kv_heads, e->cfg.head_dim, std::max(e->x_maxctx, 1),
+                                    e->cfg.builder.sliding_window);
+    pl.slots = cb::mixed_slots(e->cfg.head_dim);  // the lists' block order depends on it
     const cb::WorkListLayout lay = cb::work_list_layout(pl, e->x_ndec);
     const size_t at = (off + 3) & ~size_t(3);  // 16-byte aligned (int32 units)
     if ((int64_t)(at + lay.bytes / 4) <= e->slot_ints) {
-      const cb::WorkCounts live = cb::build_work_lists(pl, e->x_nseq, e->x_ndec, G, win, h + o_qsl, h + o_ctx,
-                                                       h + o_off, h + at, shape.split);
-      e->plan = pl;
-      e->lists.plan = shape.split ? &e->plan : nullptr;
+      const cb::WorkCounts live = cb::build_work_lists(pl, e->x_nseq, e->x_ndec, e->cfg.num_q_heads / e->cfg.num_kv_heads,
+                           e->cfg.builder.sliding_window, h + o_qsl, h + o_ctx, h + o_off, h + at);
       const uint8_t* db = reinterpret_cast<const uint8_t*>(dv + at);
       e->lists.hdr = db + lay.hdr;
       e->lists.dec_items = db + lay.dec_items;
@@ -275,7 +261,6 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
       // a recorded graph keeps its grid for every replay: it is sized by the caps
       e->lists.live_pf_items = e->capture ? -1 : live.pf_items;
       e->lists.live_dec_items = e->capture ? -1 : live.dec_items;
-      e->lists.split = !e->capture && live.split;
       e->have_lists = true;
       off = at + lay.bytes / 4;
     }
@@ -314,7 +299,6 @@ int cb_engine_load_builder(cb_engine* e, const cb_builder* src) {
 
 size_t cb_engine_workspace_bytes(const cb_engine* e) {
   if (!e || !e->pending) return 0;
-  if (e->have_lists && e->lists.plan) return e->lists.plan->bytes;  // the step's own plan (two launches)
   return cb_attention_workspace_bytes(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads, e->cfg.num_kv_heads,
                                       e->cfg.head_dim, std::max(e->x_maxctx, 1), e->cfg.dtype);
 }
@@ -357,7 +341,6 @@ int cb_engine_stats_get(const cb_engine* e, cb_engine_stats* out) {
   out->graph_captures = e->n_captures;
   out->graph_replays = e->n_replays;
   out->graphs_cached = (int64_t)e->graphs.size();
-  out->two_launch_steps = e->n_two_launch;
   return CB_OK;
 }
 
@@ -408,7 +391,6 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
     if (st == CB_OK) {
       e->pending = false;
       e->n_attended++;
-      if (e->have_lists && e->lists.split) e->n_two_launch++;
     }
     return st;
   }

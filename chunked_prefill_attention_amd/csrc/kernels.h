@@ -14,16 +14,14 @@ namespace cb {
 // null when profiling is off.  Per host thread.
 extern thread_local hipEvent_t g_prof_start;
 extern thread_local hipEvent_t g_prof_stop;
-// Recorded between the two launches of a step run as two (null: off).
-extern thread_local hipEvent_t g_prof_mid;
 // Device buffer of 4 uint64 for the main kernel's clock record (null: off).
 extern thread_local void* g_prof_clock;
 // Suspends the profiling events of this thread for a scope (graph capture).
 struct ProfileEventsOff {
-  hipEvent_t start = g_prof_start, stop = g_prof_stop, mid = g_prof_mid;
+  hipEvent_t start = g_prof_start, stop = g_prof_stop;
   void* clock = g_prof_clock;
-  ProfileEventsOff() { g_prof_start = g_prof_stop = g_prof_mid = nullptr; g_prof_clock = nullptr; }
-  ~ProfileEventsOff() { g_prof_start = start; g_prof_stop = stop; g_prof_mid = mid; g_prof_clock = clock; }
+  ProfileEventsOff() { g_prof_start = g_prof_stop = nullptr; g_prof_clock = nullptr; }
+  ~ProfileEventsOff() { g_prof_start = start; g_prof_stop = stop; g_prof_clock = clock; }
 };
 
 // Arguments of one attention step, already validated on the host.
@@ -50,7 +48,6 @@ struct Bf16Plan {
   int32_t split_pages;    // pages per decode wavefront (split-K unit)
   int32_t pf_split_keys;  // keys per prefill workgroup (split-K unit of a row tile)
   bool pf_may_split;      // some prefill row tile may need more than one split
-  bool dec_may_split;     // some decode may need more than one split
   int64_t dec_cap;        // bound on (sequence, split) decode items
   int64_t pf_tile_cap;    // bound on (sequence, 128-row tile) prefill tiles
   int64_t pf_item_cap;    // bound on (tile, key split) prefill items
@@ -67,25 +64,6 @@ int mixed_slots(int head_dim);
 Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
                    int32_t hkv, int32_t head_dim, int32_t max_context_len, int32_t window = 0);
 
-// What the host list builder knows of a step beyond its sizes (from the host
-// copies of query_start_loc, context_lens and q_offsets), and its choice of
-// one launch or two (prefill items alone, then the decode-only kernel).
-struct StepShape {
-  double dec_pages = 0;       // K/V pages the decodes read
-  double pf_pairs = 0;        // visible (query row, key) pairs of the prefill chunks, per query head
-  int64_t pf_key_tiles = 0;   // 64-key tiles over all prefill row tiles, per KV head
-  int32_t max_dec_ctx = 0, max_pf_ctx = 0;
-  bool split = false;
-};
-StepShape step_shape(int32_t num_seqs, int32_t num_decodes, int32_t group, int32_t window, const int32_t* qsl,
-                     const int32_t* ctx, const int32_t* q_off);
-// The plan of a step run as two launches: decode splits sized by the decodes'
-// own lengths, prefill key ranges by the prefill's own work.  Its workspace
-// may differ from plan_bf16's for the same sizes.
-Bf16Plan plan_bf16_two_launches(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, int32_t hq,
-                                int32_t hkv, int32_t head_dim, int32_t window, const StepShape& shape,
-                                int32_t slots);
-
 // Work lists of one bf16 step built by the caller (the engine builds them on
 // the host and uploads them with the step's metadata); when given, the
 // device plan kernel is skipped.
@@ -98,9 +76,6 @@ struct WorkLists {
   const void* pf_tiles;      // int4 [pf_tile_cap]: (sequence, row tile, first item, splits)
   const int32_t* dec_first;  // [num_decodes]
   const int32_t* dec_rem;    // [num_decodes]
-  bool split = false;        // with live counts: the prefill items in a launch of their own, then the
-                             // decode items in the decode-only kernel (see build_work_lists)
-  const Bf16Plan* plan = nullptr;  // the plan the lists were built with, when not plan_bf16's
 };
 
 // Host layout of the work lists: byte offsets inside one buffer (16-byte aligned).
@@ -114,11 +89,10 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes);
 // context_lens and q_offsets.
 struct WorkCounts {
   int64_t pf_items, dec_items;  // live prefill and decode items in the lists
-  bool split;                   // run prefill and decode as two launches (the prefill part is small)
 };
 WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t group,
                       int32_t window, const int32_t* qsl, const int32_t* ctx, const int32_t* q_off,
-                      void* dst, bool split = false);
+                      void* dst);
 
 // The same append, plus a copy of pull_bytes (a multiple of 16) from pull_src
 // (device-readable host memory) to pull_dst, done by extra blocks of the launch.

@@ -227,20 +227,11 @@ size_t cb_attention_noalloc_scratch_bytes(void);
  * enabled.  Subsequent cb_attention_step calls made by the calling thread
  * record start_event on their stream right before the main ragged attention
  * kernel and stop_event right after it, so hipEventElapsedTime gives that
- * kernel's duration alone (plan and combine kernels excluded).  An engine
- * step that runs as two launches (its prefill items, then its decode items
- * in the decode-only kernel; cb_engine_stats.two_launch_steps) gets the
- * events around both.  Passing NULL, NULL turns the hook off.  Host
- * bookkeeping only; returns CB_OK, or CB_ERR_INVALID when exactly one handle
- * is NULL.
+ * kernel's duration alone (plan and combine kernels excluded).  Passing NULL,
+ * NULL turns the hook off.  Host bookkeeping only; returns CB_OK, or
+ * CB_ERR_INVALID when exactly one handle is NULL.
  * ------------------------------------------------------------------------- */
 int cb_profile_events(void* start_event, void* stop_event);
-
-/* Companion of cb_profile_events: on a step run as two launches, mid_event
- * (a hipEvent_t with timing, as void*) is recorded between them, so that
- * start..mid times the prefill launch and mid..stop the decode launch.  NULL
- * turns it off.  Host bookkeeping only; returns CB_OK. */
-int cb_profile_split_event(void* mid_event);
 
 /* ----------------------------------------------------------------------------
  * cb_profile_clock -- clock record of the main attention kernel.
@@ -550,7 +541,6 @@ typedef struct {
   int64_t graph_captures;   /* as cb_engine_graph_stats */
   int64_t graph_replays;
   int64_t graphs_cached;
-  int64_t two_launch_steps; /* bf16 steps run as a prefill launch and a decode-only launch */
 } cb_engine_stats;
 
 /* Errors: CB_ERR_INVALID (null argument). */

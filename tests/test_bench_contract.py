@@ -46,3 +46,13 @@ def test_json_line_fields():
     assert cfg["algorithmic_kv_bytes"] > 0.9 * cfg["algorithmic_bytes"]
     # the oracle's rows agree with the GPU's within the bf16 bound the parity tests use
     assert cpu["max_abs_err_vs_gpu"] < 0.05
+
+
+@pytest.mark.gpu
+def test_windowed_mixed_step_runs():
+    """The mixed step under a 1024-token sliding window: the imported
+    histories skip the pages the builder does not hold below the window."""
+    r = _bench("--window", "1024", "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--no-clock")
+    assert r.returncode == 0, r.stderr[-2000:]
+    rec = json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1])
+    assert rec["config"]["sliding_window"] == 1024 and rec["value"] > 0
