@@ -146,6 +146,7 @@ struct Params {
   float2* pf_ml;         // [prefill item][PF_ROWS]
   float* pf_o;           // [prefill item][PF_ROWS][D]
   int32_t bt_stride;
+  const int32_t* bt_off;  // row offsets of packed block tables, or null (row s at s * bt_stride)
   int32_t num_seqs, num_decodes;
   int32_t hq, hkv, G;
   int32_t num_pages;
@@ -585,7 +586,7 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
   const int pg0 = (lo >> 4) + split * p.split_pages;
   const int pg1 = min(pg0 + p.split_pages, npages);
   const int nsplit = ((WIN ? decode_pages(ctx, p.window) : npages) + p.split_pages - 1) / p.split_pages;
-  const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+  const int32_t* btrow = p.bt + (p.bt_off ? (size_t)p.bt_off[s] : (size_t)s * p.bt_stride);
   // per-lane element offsets inside a (page, head) slab: K row hl, dims 8g + 32c;
   // V dim rows 16t + hl, keys 4g..4g+3
   const int koff = hl * D + g * 8;
@@ -832,7 +833,7 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
 
   constexpr int NK = D / 16;  // QK k-steps of 16 dims
   constexpr int NO = D / 32;  // 32-dim output tiles
-  const int32_t* btrow = p.bt + (size_t)s * p.bt_stride;
+  const int32_t* btrow = p.bt + (p.bt_off ? (size_t)p.bt_off[s] : (size_t)s * p.bt_stride);
   // LDS: two tile stages and the item's page ids.  The stages are separate
   // arrays so that the compiler can tell a copy in flight into one stage does
   // not touch the stage being read; being larger and more aligned they are
@@ -1212,6 +1213,7 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.pf_ml = reinterpret_cast<float2*>(ws + pl.off_pf_ml);
   p.pf_o = reinterpret_cast<float*>(ws + pl.off_pf_o);
   p.bt_stride = a.bt_stride;
+  p.bt_off = a.bt_offsets;
   p.num_seqs = a.num_seqs;
   p.num_decodes = a.num_decodes;
   p.hq = a.hq;

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const float* __restrict__ qrow = static_cast<const float*>(a.q) + ((size_t)t * a.hq + h) * D;
   const float* __restrict__ kc = static_cast<const float*>(a.k_cache);
   const float* __restrict__ vc = static_cast<const float*>(a.v_cache);
-  const int32_t* __restrict__ bt = a.block_tables + (size_t)s * a.bt_stride;
+  const int32_t* __restrict__ bt = a.block_tables + (a.bt_offsets ? (size_t)a.bt_offsets[s] : (size_t)s * a.bt_stride);
 
   float qv[D];
 #pragma unroll

@@ -140,7 +140,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
                         int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t page_size, int32_t num_pages, float scale, int32_t sliding_window,
                         int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                        const WorkLists* lists) {
+                        const WorkLists* lists, const int32_t* bt_offsets) {
   cb::clear_error();
   if (int st = check_common(num_kv_heads, head_dim, page_size, num_pages, dtype)) return st;
   if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
@@ -177,6 +177,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.bt_stride = block_table_stride;
+  a.bt_offsets = bt_offsets;
   a.qsl = query_start_loc;
   a.ctx_lens = context_lens;
   a.q_offsets = q_offsets;

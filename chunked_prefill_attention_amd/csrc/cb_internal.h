@@ -26,7 +26,7 @@ int attention_step_impl(const void* q, const void* k_cache, const void* v_cache,
                         int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t page_size, int32_t num_pages, float scale, int32_t sliding_window,
                         int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                        const WorkLists* lists);
+                        const WorkLists* lists, const int32_t* bt_offsets = nullptr);
 // Largest number of pages any live request of the builder holds.
 int32_t builder_max_pages_held(const cb_builder* b);
 // Deep copy of src's state into dst (dst keeps its address).

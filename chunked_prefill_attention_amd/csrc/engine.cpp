@@ -46,6 +46,7 @@ struct cb_engine {
   int64_t slot_ints = 0;
   // device views of the pending step's metadata
   const int32_t *d_qsl = nullptr, *d_ctx = nullptr, *d_off = nullptr, *d_bt = nullptr, *d_slots = nullptr;
+  const int32_t* d_btoff = nullptr;  // row offsets of the packed block tables
   // the pinned staging buffer as the device addresses it (null: not mapped,
   // then the metadata goes up with a copy in the stream)
   int32_t* meta_host_dev = nullptr;
@@ -160,7 +161,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   const int64_t stride = (int64_t)cb::builder_max_pages_held(e->builder) + cb::ceil_div(T, CB_PAGE_SIZE) + 1 +
                          (pad ? e->pad_kv / CB_PAGE_SIZE + 1 : 0);
   const int64_t bt_pages = pad ? stride : std::min<int64_t>(stride, bc.num_pages);
-  int64_t need = (B + 1) + 2 * B + B * bt_pages + T;
+  int64_t need = 2 * (B + 1) + 2 * B + B * bt_pages + T;
   if (e->cfg.dtype == CB_BF16) {  // bound of the host-built work lists (int32 units)
     const int64_t G = e->cfg.num_q_heads / e->cfg.num_kv_heads;
     const int64_t pages = bt_pages;
@@ -196,7 +197,27 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     off += n;
     return at;
   };
-  size_t o_qsl, o_ctx, o_off, o_bt, o_sl;
+  size_t o_qsl, o_ctx, o_off, o_bt, o_btoff, o_sl;
+  // block tables go up packed: row s holds the ceil(ctx / 16) pages its
+  // context covers (all the kernels read), rows back to back after an
+  // offsets array; src_row(s) is the descriptor row of launched sequence s
+  // (-1: an empty padding sequence)
+  auto put_tables = [&](int32_t nseq, auto src_row) {
+    o_btoff = off;
+    off += (size_t)nseq + 1;
+    o_bt = off;
+    int32_t acc = 0;
+    for (int32_t s = 0; s < nseq; ++s) {
+      h[o_btoff + s] = acc;
+      const int32_t r = src_row(s);
+      if (r < 0) continue;
+      const int32_t n = std::min<int32_t>((d.context_lens[r] + CB_PAGE_SIZE - 1) / CB_PAGE_SIZE, d.block_table_stride);
+      if (n > 0) std::memcpy(h + off, d.block_tables + (size_t)r * d.block_table_stride, (size_t)n * sizeof(int32_t));
+      off += n;
+      acc += n;
+    }
+    h[o_btoff + nseq] = acc;
+  };
   if (!pad || d.num_tokens == 0) {
     e->x_nseq = d.num_seqs;
     e->x_ndec = d.num_decodes;
@@ -206,7 +227,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     o_qsl = put(d.query_start_loc, (size_t)d.num_seqs + 1);
     o_ctx = put(d.context_lens, (size_t)d.num_seqs);
     o_off = put(d.q_offsets, (size_t)d.num_seqs);
-    o_bt = put(d.block_tables, (size_t)d.num_seqs * d.block_table_stride);
+    put_tables(d.num_seqs, [](int32_t s) { return s; });
     o_sl = put(d.slot_mapping, (size_t)d.num_tokens);
   } else {
     // padded shape: [decodes | empty | prefills | empty], tokens past the real
@@ -230,12 +251,10 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     for (int32_t s = 0; s < B_p; ++s) h[off++] = src_of(s) >= 0 ? d.context_lens[src_of(s)] : 0;
     o_off = off;
     for (int32_t s = 0; s < B_p; ++s) h[off++] = src_of(s) >= 0 ? d.q_offsets[src_of(s)] : 0;
-    o_bt = off;
-    for (int32_t s = 0; s < B_p; ++s) {
-      const int32_t r = src_of(s);
-      for (int32_t i = 0; i < e->x_stride; ++i)
-        h[off++] = (r >= 0 && i < d.block_table_stride) ? d.block_tables[(size_t)r * d.block_table_stride + i] : 0;
-    }
+    put_tables(B_p, src_of);
+    // a padded shape keeps the padded tables' room, so that its metadata
+    // layout and upload size (which a recorded graph holds) do not change
+    off = o_bt + (size_t)B_p * e->x_stride;
     o_sl = put(d.slot_mapping, (size_t)d.num_tokens);
     for (int32_t t = d.num_tokens; t < e->x_ntok; ++t) h[off++] = -1;
   }
@@ -285,6 +304,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
   e->d_ctx = dv + o_ctx;
   e->d_off = dv + o_off;
   e->d_bt = dv + o_bt;
+  e->d_btoff = dv + o_btoff;
   e->d_slots = dv + o_sl;
   *out = d;
   return CB_OK;
@@ -375,7 +395,7 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
                                    e->x_nseq, e->x_ndec, e->x_ntok, e->x_maxctx, c.num_q_heads,
                                    c.num_kv_heads, c.head_dim, CB_PAGE_SIZE, c.builder.num_pages, c.scale,
                                    c.builder.sliding_window, c.dtype, out, c.workspace, c.workspace_bytes,
-                                   stream, e->have_lists ? &e->lists : nullptr);
+                                   stream, e->have_lists ? &e->lists : nullptr, e->d_btoff);
   };
   // with the pull, the staging slot is free once the append kernel has run
   auto staged = [&]() {

@@ -31,6 +31,9 @@ struct AttnArgs {
   const void* v_cache;
   const int32_t* block_tables;
   int32_t bt_stride;
+  // row s of the block tables starts at bt_offsets[s] when set (rows packed
+  // back to back, each as long as its context), else at s * bt_stride
+  const int32_t* bt_offsets;
   const int32_t* qsl;
   const int32_t* ctx_lens;
   const int32_t* q_offsets;
