@@ -35,7 +35,10 @@
 // Block order: the work lists start with the live item counts; live blocks
 // run first (prefill first when its workgroups fit in one round of the
 // device's slots, else prefill and decode alternating) and blocks past the
-// live work return at once.
+// live work return at once.  When the host built the lists and the prefill
+// part is a large share of the step, the kinds go by CU instead: workgroups
+// that land on the first k CUs of each shader engine take prefill units, the
+// rest decode units, each from per-XCD claim queues (see pick_unit).
 //
 // Layouts: K pages are token-major ([16][D] per (page, head)), so a lane's
 // MFMA A-operand (one key, 8 consecutive dims) is one 16-byte load.  V pages
@@ -59,6 +62,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 
 #include "kernels.h"
 
@@ -340,6 +344,24 @@ __host__ __device__ __forceinline__ int tile_splits(int tile, int L, int G, int 
 // rounds, going first would run the MFMA-bound and the HBM-bound work one
 // after the other, so prefill and decode blocks are interleaved instead and
 // most CUs hold one of each.
+// The work lists' header: (live prefill items, live decode items, block
+// order, prefill CUs per shader engine) and then, for the CU split, one
+// claim counter per XCD for each kind (zero when the launch starts).
+constexpr int N_XCD = 8;
+struct UnitQueues {
+  int next_pf[N_XCD];
+  int next_dec[N_XCD];
+};
+constexpr size_t HDR_BYTES = 16 + sizeof(UnitQueues);
+#ifndef CB_CU_SPLIT         // host-built lists: prefill and decode blocks pick their kind by the CU they land on
+#define CB_CU_SPLIT 1
+#endif
+#ifndef CB_CU_SPLIT_MIN     // split only when the prefill part earns at least this many CUs per shader engine
+#define CB_CU_SPLIT_MIN 3
+#endif
+#ifndef CB_CU_SPLIT_MAX     // at most this many prefill CUs per shader engine (of 8)
+#define CB_CU_SPLIT_MAX 6
+#endif
 __host__ __device__ inline int mix_order(int64_t pf_live_items, int64_t dec_live_items, int hkv, int slots) {
   return (pf_live_items * hkv > slots && dec_live_items > 0) ? 1 : 0;
 }
@@ -471,6 +493,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(Params p) {
   if (tid == 0) {
     const int pl = min(icarry, p.pf_item_cap), dl = min(dec_total, p.dec_cap);
     *p.hdr = make_int4(pl, dl, mix_order(pl, dl, p.hkv, p.slots), 0);
+    UnitQueues* uq = reinterpret_cast<UnitQueues*>(p.hdr + 1);
+    for (int x = 0; x < N_XCD; ++x) uq->next_pf[x] = uq->next_dec[x] = 0;
   }
 }
 
@@ -1028,6 +1052,41 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
 // four decode wavefronts each.  The no-prefill instantiation needs neither
 // LDS nor the prefill registers and runs at higher occupancy.
 // ---------------------------------------------------------------------------
+// CU split: a unit of one kind, numbered i, belongs to XCD i % 8 (blocks
+// are dealt to the XCDs round-robin, so prefill unit i keeps its KV head's
+// XCD); a workgroup claims the next unit of its XCD's queue, then of the
+// other XCDs' queues.  -1: every unit of this kind is taken.
+__device__ __forceinline__ int take_unit(int* next, int n, int xcc) {
+  for (int k = 0; k < N_XCD; ++k) {
+    const int x = (xcc + k) & (N_XCD - 1);
+    const int cnt = n > x ? (n - x + N_XCD - 1) / N_XCD : 0;
+    if (cnt == 0) continue;
+    const int q = atomicAdd(&next[x], 1);
+    if (q < cnt) return x + N_XCD * q;
+  }
+  return -1;
+}
+// Workgroups on CUs 1..k of each shader engine take prefill units, the
+// others decode units; either kind falls back to the other when its own is
+// used up.  The launch holds exactly as many workgroups as units, so every
+// workgroup gets one.  Returns the prefill unit, -2 - (decode unit), or -1.
+__device__ int pick_unit(const Params& p, int lp, int ld, int k) {
+  const unsigned hw = (unsigned)__builtin_amdgcn_s_getreg(63492);          // HW_ID
+  const int xcc = (int)((unsigned)__builtin_amdgcn_s_getreg(63508) & 7u);  // XCC_ID
+  const int cu = (int)((hw >> 8) & 15u);
+  UnitQueues* q = reinterpret_cast<UnitQueues*>(p.hdr + 1);
+  if (cu >= 1 && cu <= k) {
+    const int r = take_unit(q->next_pf, lp, xcc);
+    if (r >= 0) return r;
+    const int d = take_unit(q->next_dec, ld, xcc);
+    return d >= 0 ? -2 - d : -1;
+  }
+  const int d = take_unit(q->next_dec, ld, xcc);
+  if (d >= 0) return -2 - d;
+  const int r = take_unit(q->next_pf, lp, xcc);
+  return r >= 0 ? r : -1;
+}
+
 template <int D, bool WIN>
 __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kernel(Params p) {
   const int b = blockIdx.x;
@@ -1038,7 +1097,16 @@ __global__ __launch_bounds__(PF_THREADS, 512 / PF_THREADS) void attn_mixed_kerne
   const int lp = min(h.x * p.hkv, np);
   const int ld = min((h.y * p.hkv + PF_WAVES - 1) / PF_WAVES, nd);
   int pf = -1, dec = -1;
-  if (b < lp + ld) {
+  if (CB_CU_SPLIT && h.w > 0 && lp > 0 && ld > 0) {
+    if (b >= lp + ld) return;
+    __shared__ int picked;
+    if (threadIdx.x == 0) picked = pick_unit(p, lp, ld, h.w);
+    __syncthreads();
+    const int r = picked;
+    if (r >= 0) pf = r;
+    else if (r <= -2) dec = -2 - r;
+    else return;
+  } else if (b < lp + ld) {
     // interleaved: groups of 8 alternate; blocks go to the XCDs round-robin,
     // so every prefill index stays on the XCD it has in prefill-first order
     const int m8 = h.z ? (min(lp, ld) & ~7) : 0;
@@ -1347,7 +1415,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   pl.hkv = hkv;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   size_t off = 0;
-  pl.off_hdr = off;         off = align(off + 16);
+  pl.off_hdr = off;         off = align(off + HDR_BYTES);
   pl.off_dec_items = off;   off = align(off + (size_t)pl.dec_cap * 16);
   pl.off_pf_items = off;    off = align(off + (size_t)pl.pf_item_cap * 16);
   pl.off_pf_tiles = off;    off = align(off + (size_t)pl.pf_tile_cap * 16);
@@ -1374,7 +1442,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
   auto align = [](size_t x) { return (x + 15) & ~size_t(15); };
   WorkListLayout L{};
   size_t off = 0;
-  L.hdr = off;        off = align(off + 16);
+  L.hdr = off;        off = align(off + HDR_BYTES);
   L.dec_items = off;  off = align(off + (size_t)pl.dec_cap * 16);
   L.pf_items = off;   off = align(off + (size_t)pl.pf_item_cap * 16);
   L.pf_tiles = off;   off = align(off + (size_t)pl.pf_tile_cap * 16);
@@ -1451,8 +1519,25 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
   for (int64_t i = nt; i < pl.pf_tile_cap; ++i) pft[i] = make_int4(-1, 0, 0, 0);
   for (int64_t i = ni; i < pl.pf_item_cap; ++i) pfi[i] = make_int4(-1, 0, 0, 0);
   const int64_t pl_live = std::min<int64_t>(ni, pl.pf_item_cap), dl_live = std::min<int64_t>(n, pl.dec_cap);
+  // CU split: prefill CUs per shader engine (of 8) in proportion to the
+  // prefill part's share of the step's estimated time (MFMA work at ~0.95
+  // PFLOP/s, K/V bytes at ~6 TB/s; head size and KV heads cancel out)
+  int k = 0;
+  if (CB_CU_SPLIT && pl_live > 0 && dl_live > 0) {
+    double pairs = 0, pages = 0;
+    for (int s = 0; s < num_decodes; ++s) pages += decode_pages(ctx[s], window);
+    for (int s = num_decodes; s < num_seqs; ++s)
+      for (int i = 0; i < qsl[s + 1] - qsl[s]; ++i) {
+        const int64_t pos = (int64_t)q_off[s] + i;
+        pairs += (double)(window > 0 ? std::min<int64_t>(pos + 1, window) : pos + 1);
+      }
+    const double t_pf = pairs * 4.0 * G / 0.95e15, t_dec = pages * 64.0 / 6.0e12;
+    k = std::min(CB_CU_SPLIT_MAX, std::max(1, (int)std::lround(8.0 * t_pf / (t_pf + t_dec))));
+    if (k < CB_CU_SPLIT_MIN) k = 0;  // a small prefill part: the block order above
+  }
   *reinterpret_cast<int4*>(base + L.hdr) =
-      make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), 0);
+      make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), k);
+  std::memset(base + L.hdr + 16, 0, sizeof(UnitQueues));
   return WorkCounts{pl_live, dl_live};
 }
 
