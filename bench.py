@@ -244,7 +244,9 @@ def main():
     stops = [TimingEvent() for _ in range(args.steps)]
     span0 = [TimingEvent() for _ in range(args.steps)]
     span1 = [TimingEvent() for _ in range(args.steps)]
-    for e in starts + stops + span0 + span1:
+    mid0 = [TimingEvent() for _ in range(args.steps)]   # span pass: the main kernel's start and end too
+    mid1 = [TimingEvent() for _ in range(args.steps)]
+    for e in starts + stops + span0 + span1 + mid0 + mid1:
         e.record()
     stream = layer.graph_stream if layer.graphs else torch.cuda.current_stream(dev)
 
@@ -263,12 +265,14 @@ def main():
             return
         if k is not None:     # timed steps: events around the main kernel only
             lib.cb_profile_events(starts[k].cuda_event, stops[k].cuda_event)
-        elif span is not None:  # the span pass: events around the whole step
+        elif span is not None:  # the span pass: events around the whole step and the main kernel
             span0[span].record(stream)
+            lib.cb_profile_events(mid0[span].cuda_event, mid1[span].cuda_event)
         layer.attend(q, kn, vn, out=out, stream=stream)        # a3 .. a7
         if k is not None:
             lib.cb_profile_events(None, None)
         elif span is not None:
+            lib.cb_profile_events(None, None)
             span1[span].record(stream)
 
     for i in range(args.warmup):
@@ -290,6 +294,10 @@ def main():
             one_step(span=k)
         torch.cuda.synchronize()
         span_ms = [s.elapsed_time(e) for s, e in zip(span0, span1)]
+        # the step's other launches: append (with the metadata pull) before the
+        # main kernel, combine after it, each with its launch gap
+        append_us = float(np.mean([s.elapsed_time(m) for s, m in zip(span0, mid0)])) * 1e3
+        combine_us = float(np.mean([m.elapsed_time(e) for m, e in zip(mid1, span1)])) * 1e3
     span_s = float(np.mean(span_ms)) / 1e3
     if cold:              # the wall clock includes the flushes: a step is its device span
         step_s = span_s
@@ -313,6 +321,9 @@ def main():
     roof["kernel_us"] = round(kern_s * 1e6, 2)
     roof["step_roofline_frac"] = round(max(t_hbm, t_mfma) / step_s, 4)
     roof["device_span_us"] = round(span_s * 1e6, 2)   # kv_append .. combine on the device
+    if not layer.graphs:
+        roof["append_us"] = round(append_us, 2)        # kv_append (+ metadata pull), up to the main kernel
+        roof["combine_us"] = round(combine_us, 2)      # after the main kernel: split-K combine
     pct = lambda xs, q: round(float(np.percentile(xs, q)) * 1e3, 2)
     roof["kernel_us_p10_p50_p90"] = [pct(kern_ms, 10), pct(kern_ms, 50), pct(kern_ms, 90)]
     roof["span_us_p10_p50_p90"] = [pct(span_ms, 10), pct(span_ms, 50), pct(span_ms, 90)]
