@@ -1302,8 +1302,13 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.dec_blocks = (int32_t)dec_blocks;
   p.slots = pl.slots > 0 ? pl.slots : mixed_slots(D);
   const bool dec_splits = a.num_decodes > 0 && (int64_t)pl.split_pages * 16 < a.max_context_len;
-  const int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
-  const int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv * (PF_ROWS / CP_ROWS) : 0;
+  int64_t comb_dec = dec_splits ? ((int64_t)a.num_decodes * a.hq + 3) / 4 : 0;
+  int64_t comb_pf = pl.pf_may_split ? pl.pf_tile_cap * a.hkv * (PF_ROWS / CP_ROWS) : 0;
+  if (lists && lists->live_pf_items >= 0 && lists->live_dec_items >= 0) {
+    // the caller's lists say which kinds actually split this step
+    if (!lists->dec_split) comb_dec = 0;
+    if (!lists->pf_split) comb_pf = 0;
+  }
   p.comb_dec_blocks = (int32_t)comb_dec;
 
   if (lists) {  // built by the caller: read them where they were uploaded
@@ -1457,6 +1462,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes) {
 // length), prefill tiles heaviest (last) first with their key splits.
 WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t G, int32_t window,
                       const int32_t* qsl, const int32_t* ctx, const int32_t* q_off, void* dst) {
+  bool any_pf_split = false, any_dec_split = false;
   const WorkListLayout L = work_list_layout(pl, num_decodes);
   uint8_t* base = static_cast<uint8_t*>(dst);
   int4* dec = reinterpret_cast<int4*>(base + L.dec_items);
@@ -1470,6 +1476,7 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
   for (int s = 0; s < num_decodes; ++s) {
     const int np = decode_pages(ctx[s], window);
     const int nfull = np / SP, rem = np - nfull * SP;
+    any_dec_split = any_dec_split || np > SP;
     first[s] = (int32_t)n;
     for (int k = 0; k < nfull && n < pl.dec_cap; ++k) dec[n++] = make_int4(s, k, ctx[s], qsl[s]);
     if (rem > 0) counts[SP - rem]++;
@@ -1503,6 +1510,7 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
       ++nt;
       ni += tns[k];
       maxns = std::max(maxns, tns[k]);
+      any_pf_split = any_pf_split || tns[k] > 1;
     }
     int64_t it = base;
     for (int ks = 0; ks < maxns; ++ks) {  // items split-major
@@ -1538,7 +1546,7 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
   *reinterpret_cast<int4*>(base + L.hdr) =
       make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), k);
   std::memset(base + L.hdr + 16, 0, sizeof(UnitQueues));
-  return WorkCounts{pl_live, dl_live};
+  return WorkCounts{pl_live, dl_live, any_pf_split, any_dec_split};
 }
 
 }  // namespace cb

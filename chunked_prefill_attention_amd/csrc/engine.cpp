@@ -280,6 +280,8 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
       // a recorded graph keeps its grid for every replay: it is sized by the caps
       e->lists.live_pf_items = e->capture ? -1 : live.pf_items;
       e->lists.live_dec_items = e->capture ? -1 : live.dec_items;
+      e->lists.pf_split = live.pf_split;
+      e->lists.dec_split = live.dec_split;
       e->have_lists = true;
       off = at + lay.bytes / 4;
     }

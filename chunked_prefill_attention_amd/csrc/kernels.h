@@ -74,6 +74,8 @@ struct WorkLists {
   const void* hdr;           // int4: (live prefill items, live decode items, block order, 0)
   int64_t live_pf_items = -1;   // when >= 0 (the caller built the lists and is not recording a
   int64_t live_dec_items = -1;  // graph), the launch sizes its grid to the live work
+  bool pf_split = true;         // with live counts: whether any prefill tile / decode has more than
+  bool dec_split = true;        // one split (the combine launch skips the kind that has none)
   const void* dec_items;     // int4 [dec_cap]: (sequence, split, context, query row); -1 = none
   const void* pf_items;      // int4 [pf_item_cap]: (sequence, row tile, key split, partial slot)
   const void* pf_tiles;      // int4 [pf_tile_cap]: (sequence, row tile, first item, splits)
@@ -92,6 +94,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes);
 // context_lens and q_offsets.
 struct WorkCounts {
   int64_t pf_items, dec_items;  // live prefill and decode items in the lists
+  bool pf_split, dec_split;     // some prefill row tile / some decode has more than one split
 };
 WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t group,
                       int32_t window, const int32_t* qsl, const int32_t* ctx, const int32_t* q_off,
