@@ -139,7 +139,8 @@ struct Params {
   const int32_t* ctx_lens;
   const int32_t* q_off;
   uint16_t* out;
-  int4* hdr;             // (live prefill items, live decode items, block order, 0)
+  int4* hdr;             // (live prefill items, live decode items, block order, prefill CUs per SE),
+                         // then the CU split's claim queues (UnitQueues)
   int4* dec_items;       // (sequence, split, context length, query row); sequence -1 = no work
   int4* pf_items;        // (sequence, row tile, key split, partial slot); -1 = no work
   int4* pf_tiles;        // (sequence, row tile, first item, number of splits); -1 = none

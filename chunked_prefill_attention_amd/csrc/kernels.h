@@ -71,7 +71,8 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
 // the host and uploads them with the step's metadata); when given, the
 // device plan kernel is skipped.
 struct WorkLists {
-  const void* hdr;           // int4: (live prefill items, live decode items, block order, 0)
+  const void* hdr;           // int4 (live prefill items, live decode items, block order, prefill CUs per
+                             // shader engine), then the CU split's claim queues (zero)
   int64_t live_pf_items = -1;   // when >= 0 (the caller built the lists and is not recording a
   int64_t live_dec_items = -1;  // graph), the launch sizes its grid to the live work
   bool pf_split = true;         // with live counts: whether any prefill tile / decode has more than
