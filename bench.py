@@ -353,6 +353,10 @@ def main():
         ach = achievable_read_gbs(max(bytes_alg, 1 << 30))
         roof["achievable_read_GBps"] = ach
         roof["frac_of_achievable"] = round(roof["achieved"] / ach, 4) if ach else None
+    elif not args.no_clock:      # beside the peak: a plain bf16 GEMM of the vendor BLAS
+        ach = achievable_gemm_tflops(dev)
+        roof["achievable_gemm_TFLOPs"] = ach
+        roof["frac_of_achievable"] = round(roof["achieved"] / ach, 4) if ach else None
     log(f"[bench] host enqueue {(t_enq - t0) / args.steps * 1e3:.3f} ms/step")
     log(f"[bench] device span (append .. combine) {span_s * 1e6:.1f} us")
     log(f"[bench] step {step_s * 1e3:.3f} ms, attention kernel {kern_s * 1e6:.1f} us, "
@@ -520,6 +524,30 @@ def achievable_read_gbs(nbytes):
         r = subprocess.run([probe, "read", str(nbytes), "10"], capture_output=True, text=True, timeout=120)
         return float(json.loads(r.stdout.strip().splitlines()[-1])["GBps"]) if r.returncode == 0 else None
     except (subprocess.SubprocessError, ValueError, KeyError, IndexError):
+        return None
+
+
+def achievable_gemm_tflops(dev, n=16384, reps=5):
+    """TFLOP/s of a plain bf16 GEMM (n x n x n, the vendor BLAS behind torch.matmul,
+    contiguous operands) on this GPU: the dense-matrix rate the chip sustains
+    in practice (the largest of 4096..16384 cubes measured best), for comparison
+    with MFMA-bound kernels.  None on failure."""
+    import torch
+    try:
+        a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+        b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+        c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = TimingEvent(), TimingEvent()
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del a, b, c
+        return round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    except Exception:  # pragma: no cover
         return None
 
 
