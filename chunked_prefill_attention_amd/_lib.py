@@ -54,7 +54,8 @@ class EngineConfig(C.Structure):
 
 class EngineStats(C.Structure):
     _fields_ = [("steps_scheduled", i64), ("steps_attended", i64), ("slot_waits", i64),
-                ("graph_captures", i64), ("graph_replays", i64), ("graphs_cached", i64)]
+                ("graph_captures", i64), ("graph_replays", i64), ("graphs_cached", i64),
+                ("cu_split_steps", i64)]
 
 
 # name -> (restype, argtypes); one line per declaration of include/cb.h

@@ -1547,7 +1547,7 @@ WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_de
   *reinterpret_cast<int4*>(base + L.hdr) =
       make_int4((int)pl_live, (int)dl_live, mix_order(pl_live, dl_live, pl.hkv, pl.slots), k);
   std::memset(base + L.hdr + 16, 0, sizeof(UnitQueues));
-  return WorkCounts{pl_live, dl_live, any_pf_split, any_dec_split};
+  return WorkCounts{pl_live, dl_live, any_pf_split, any_dec_split, k};
 }
 
 }  // namespace cb

@@ -70,7 +70,7 @@ const char* cb_status_string(int status) {
 
 const char* cb_last_error(void) { return cb::g_err; }
 
-int cb_abi_version(void) { return 3; }
+int cb_abi_version(void) { return 4; }
 
 int cb_profile_events(void* start_event, void* stop_event) {
   cb::clear_error();

@@ -63,6 +63,8 @@ struct cb_engine {
   int64_t n_captures = 0, n_replays = 0;
   int64_t n_scheduled = 0, n_attended = 0;
   int64_t n_slot_waits = 0;  // schedules whose staging slot was still being read, and waited
+  int64_t n_cu_split = 0;    // attended steps whose lists chose the CU split
+  bool step_cu_split = false;
   void drop_graphs() {
     for (auto& kv : graphs) (void)hipGraphExecDestroy(kv.second);
     graphs.clear();
@@ -259,6 +261,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
     for (int32_t t = d.num_tokens; t < e->x_ntok; ++t) h[off++] = -1;
   }
   e->have_lists = false;
+  e->step_cu_split = false;
   if (e->cfg.dtype == CB_BF16 && e->x_ntok > 0) {
     // the attention step's work lists, built here instead of by a device plan kernel
     cb::Bf16Plan pl = cb::plan_bf16(e->x_nseq, e->x_ndec, e->x_ntok, e->cfg.num_q_heads,
@@ -281,6 +284,7 @@ int cb_engine_schedule(cb_engine* e, void* stream, cb_step* out) {
       e->lists.live_pf_items = e->capture ? -1 : live.pf_items;
       e->lists.live_dec_items = e->capture ? -1 : live.dec_items;
       e->lists.pf_split = live.pf_split;
+      e->step_cu_split = live.cu_split > 0;
       e->lists.dec_split = live.dec_split;
       e->have_lists = true;
       off = at + lay.bytes / 4;
@@ -363,6 +367,7 @@ int cb_engine_stats_get(const cb_engine* e, cb_engine_stats* out) {
   out->graph_captures = e->n_captures;
   out->graph_replays = e->n_replays;
   out->graphs_cached = (int64_t)e->graphs.size();
+  out->cu_split_steps = e->n_cu_split;
   return CB_OK;
 }
 
@@ -413,6 +418,7 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
     if (st == CB_OK) {
       e->pending = false;
       e->n_attended++;
+      if (e->have_lists && e->step_cu_split) e->n_cu_split++;
     }
     return st;
   }
@@ -448,6 +454,7 @@ int cb_engine_attend(cb_engine* e, const void* q, const void* k_new, const void*
   if (st == CB_OK) {
     e->pending = false;
     e->n_attended++;
+    if (e->have_lists && e->step_cu_split) e->n_cu_split++;
   }
   return st;
 }

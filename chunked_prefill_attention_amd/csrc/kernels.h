@@ -96,6 +96,7 @@ WorkListLayout work_list_layout(const Bf16Plan& pl, int32_t num_decodes);
 struct WorkCounts {
   int64_t pf_items, dec_items;  // live prefill and decode items in the lists
   bool pf_split, dec_split;     // some prefill row tile / some decode has more than one split
+  int cu_split;                 // prefill CUs per shader engine chosen for the CU split (0: none)
 };
 WorkCounts build_work_lists(const Bf16Plan& pl, int32_t num_seqs, int32_t num_decodes, int32_t group,
                       int32_t window, const int32_t* qsl, const int32_t* ctx, const int32_t* q_off,

@@ -541,6 +541,8 @@ typedef struct {
   int64_t graph_captures;   /* as cb_engine_graph_stats */
   int64_t graph_replays;
   int64_t graphs_cached;
+  int64_t cu_split_steps;   /* bf16 steps whose prefill and decode workgroups took their kind
+                               by the CU they ran on (a large prefill share of the step) */
 } cb_engine_stats;
 
 /* Errors: CB_ERR_INVALID (null argument). */

@@ -30,7 +30,7 @@ def test_status_strings_and_version():
     lib = _lib.load()
     assert lib.cb_status_string(0) == b"CB_OK"
     assert lib.cb_status_string(-3) == b"CB_ERR_WORKSPACE"
-    assert lib.cb_abi_version() == 3
+    assert lib.cb_abi_version() == 4
 
 
 NULL = C.c_void_p(0)

@@ -142,6 +142,11 @@ def test_long_prompt_forty_steps():
         if k in (0, 1, 19, 38, 39):
             err = max(err, r.check(desc, q, out, rng_seed=k))
         say(f"  step {k}: chunk at {desc.q_offsets[-1]}, max abs err {err:.2e}")
+    # the later chunks are a large share of their steps: those run with the
+    # prefill and decode workgroups split by CU (and were checked above)
+    n = r.layer.stats()["cu_split_steps"]
+    say(f"  {n} of 40 steps split by CU")
+    assert 0 < n < 40
 
 
 def _bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -260,3 +265,6 @@ def test_fifo_trace_every_step():
     say(f"  trace done: {step} steps, {appended} appended tokens read back, {checked_rows} rows x {hq} heads "
         f"checked, mean fragmentation {np.mean(frag):.4f}")
     assert L.builder.stats()["total_finished"] == len(reqs)
+    n = L.stats()["cu_split_steps"]
+    say(f"  {n} of {step} steps split by CU")
+    assert 0 < n < step
