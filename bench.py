@@ -86,6 +86,32 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(self._h)
 
 
+class CacheFlush:
+    """Empties the L2 and Infinity Cache of a step's data before a cold step.
+
+    write: every byte of a 1 GiB buffer is written (the dirty lines it leaves
+    are written back while the next step evicts them, so that step also pays
+    up to the caches' size in extra HBM writes).  read: a 1 GiB buffer,
+    written once here, is read through by a sum; the caches then hold only
+    clean lines of unrelated data, and the step's own traffic is all it
+    moves."""
+
+    def __init__(self, mode, dev):
+        import torch
+        self.mode = mode
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        self.buf.fill_(1)
+        self.acc = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def __call__(self, k, stream):
+        import torch
+        with torch.cuda.stream(stream):
+            if self.mode == "write":
+                self.buf.fill_(k & 255)
+            else:
+                torch.sum(self.buf.view(torch.int64), dim=0, out=self.acc)
+
+
 def workload(name):
     import workloads as wl
     if name == "mixed":
@@ -148,53 +174,13 @@ def algorithmic(desc, hq, hkv, d, esize, window=0):
     return kv + qo + meta, flops, int(pairs.sum()), kv
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixed", choices=["mixed", "decode", "long", "chunk", "trace"],
-                    help="trace: the 256-request FIFO trace run once, every step timed cold")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--trace-csv", default="", help="trace workload: also write one CSV row per step here")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
-    ap.add_argument("--page-order", default="shuffled", choices=["shuffled", "sequential"],
-                    help="physical page ids: a seeded random permutation (default) or handed out in order")
-    ap.add_argument("--graphs", default="",
-                    help="Q,KV padding intervals: replay each padded step shape from a recorded HIP graph")
-    ap.add_argument("--cold", default="auto", choices=["auto", "on", "off"],
-                    help="write a 1 GiB scratch buffer before every timed step so that no cache level holds "
-                         "the step's data (auto: on when the step moves less than 1 GB); the step time is then "
-                         "the device span of each step")
-    ap.add_argument("--no-clock", action="store_true",
-                    help="skip the shader-clock measurement of MFMA-bound steps (40 extra back-to-back calls)")
-    ap.add_argument("--window", type=int, default=0,
-                    help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: there is no multi-GPU path here "
-              "(the attention step would shard by sequence or by KV head, with no exchange between GPUs).",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-    import chunked_prefill_attention_amd as cb
+def prepare_layer(w, args, dev, gq=0, gkv=0):
+    """The workload's engine layer with every request submitted and its cached
+    history imported; returns the layer and the per-request K/V histories."""
     from chunked_prefill_attention_amd.engine import PagedAttentionLayer
     import workloads as wl
-
-    cb.load()
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    if args.workload == "trace":
-        return run_trace(args, dev)
-    w, advance = workload(args.workload)
-    if args.window > 0:
-        w.name += f"_window{args.window}"
-    gq, gkv = (int(x) for x in args.graphs.split(",")) if args.graphs else (0, 0)
-    hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
-    t_setup = time.perf_counter()
-    layer = PagedAttentionLayer(hq, hkv, d, w.pool_pages, w.max_batch_tokens, w.max_requests, w.dtype,
+    hkv, d = w.n_kv_heads, w.head_dim
+    layer = PagedAttentionLayer(w.n_q_heads, hkv, d, w.pool_pages, w.max_batch_tokens, w.max_requests, w.dtype,
                                 w.max_prefill_chunk, w.safety_margin,
                                 page_shuffle_seed=w.seed if args.page_order == "shuffled" else 0, device=dev,
                                 sliding_window=args.window, graph_q_interval=gq, graph_kv_interval=gkv)
@@ -212,6 +198,65 @@ def main():
         lo = min(first_held_position(layer.builder, i), c)
         if lo < c:
             layer.write_positions(i, lo, c, k[lo:c], v[lo:c])
+    return layer, hist
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed", choices=["mixed", "decode", "long", "chunk", "trace"],
+                    help="trace: the 256-request FIFO trace run once, every step timed cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-csv", default="", help="trace workload and --sweep: also write one CSV row per step here")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle leg")
+    ap.add_argument("--page-order", default="shuffled", choices=["shuffled", "sequential"],
+                    help="physical page ids: a seeded random permutation (default) or handed out in order")
+    ap.add_argument("--graphs", default="",
+                    help="Q,KV padding intervals: replay each padded step shape from a recorded HIP graph")
+    ap.add_argument("--cold", default="auto", choices=["auto", "on", "off"],
+                    help="empty the caches (1 GiB written or read, --flush) before every timed step so that no cache level holds "
+                         "the step's data (auto: on when the step moves less than 1 GB); the step time is then "
+                         "the device span of each step")
+    ap.add_argument("--flush", default="read", choices=["read", "write"],
+                    help="how a cold step's caches are emptied: write 1 GiB (its dirty lines are written back "
+                         "during the step) or read 1 GiB (clean lines only)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock measurement of MFMA-bound steps (40 extra back-to-back calls)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="long / chunk workloads: time every step that carries a chunk of the 20,000-token "
+                         "prompt (40 steps), each --steps times cold after --warmup untimed runs")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (row p sees keys p-W < j <= p); 0 = full attention")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path here "
+              "(the attention step would shard by sequence or by KV head, with no exchange between GPUs).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_prefill_attention_amd as cb
+    import workloads as wl
+
+    if args.sweep and args.workload not in ("long", "chunk"):
+        raise SystemExit("--sweep applies to the long and chunk workloads")
+    cb.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.workload == "trace":
+        return run_trace(args, dev)
+    w, advance = workload(args.workload)
+    if args.window > 0:
+        w.name += f"_window{args.window}"
+    if args.sweep:
+        return run_sweep(args, dev, w)
+    gq, gkv = (int(x) for x in args.graphs.split(",")) if args.graphs else (0, 0)
+    hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+    t_setup = time.perf_counter()
+    layer, hist = prepare_layer(w, args, dev, gq, gkv)
     for _ in range(advance):                       # earlier steps: append only
         desc = layer.schedule()
         ks = torch.cat([hist[int(r)][0][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
@@ -239,7 +284,7 @@ def main():
     bytes_alg, flops_alg, pairs, kv_alg = algorithmic(desc0, hq, hkv, d, esize, args.window)
     lib = cb.load()
     cold = args.cold == "on" or (args.cold == "auto" and bytes_alg < 1e9)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold else None
+    flush = CacheFlush(args.flush, dev) if cold else None
     starts = [TimingEvent() for _ in range(args.steps)]
     stops = [TimingEvent() for _ in range(args.steps)]
     span0 = [TimingEvent() for _ in range(args.steps)]
@@ -250,10 +295,9 @@ def main():
         e.record()
     stream = layer.graph_stream if layer.graphs else torch.cuda.current_stream(dev)
 
-    def one_step(k=None, flush=True, span=None):
-        if cold and flush:                                     # evict the step's data from L2 and MALL
-            with torch.cuda.stream(stream):
-                scratch.fill_(k or 0)
+    def one_step(k=None, flush_first=True, span=None):
+        if cold and flush_first:                               # evict the step's data from L2 and MALL
+            flush(k or 0, stream)
         layer.load_builder(snapshot)                           # same starting state each time
         layer.schedule(stream=stream)                          # a1 + a2
         if layer.graphs:                                       # events around the whole graph
@@ -327,7 +371,8 @@ def main():
     pct = lambda xs, q: round(float(np.percentile(xs, q)) * 1e3, 2)
     roof["kernel_us_p10_p50_p90"] = [pct(kern_ms, 10), pct(kern_ms, 50), pct(kern_ms, 90)]
     roof["span_us_p10_p50_p90"] = [pct(span_ms, 10), pct(span_ms, 50), pct(span_ms, 90)]
-    roof["timing"] = ("cold: 1 GiB written before each step; step = device span" if cold
+    roof["timing"] = (f"cold: 1 GiB {'written' if args.flush == 'write' else 'read'} before each step; "
+                      "step = device span" if cold
                       else "warm: steps back to back; step = wall time; HIP events around the main kernel only "
                            "(the device span from a second pass with events around each step)")
     if roof["bound"] == "mfma" and not args.no_clock:  # the shader clock the chip holds under this load
@@ -387,7 +432,7 @@ def main():
 def run_trace(args, dev):
     """The FIFO trace (256 requests: Poisson arrivals, lognormal prompts,
     geometric outputs; pool 200,000 pages; 64q/8kv, D 128, bf16) run once
-    through the engine.  Every step is timed once, cold (1 GiB written before
+    through the engine.  Every step is timed once, cold (1 GiB written or read before
     it), as its device span (append .. combine), and classified HBM- or
     MFMA-bound by its algorithmic bytes and flops."""
     import numpy as np
@@ -400,7 +445,7 @@ def run_trace(args, dev):
     layer = PagedAttentionLayer(hq, hkv, d, 200_000, 2048, 128, dtype, 0, 0.15, page_shuffle_seed=5, device=dev)
     lib = cb.load()
     stream = torch.cuda.current_stream(dev)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(args.flush, dev)
     ev = [TimingEvent() for _ in range(4)]
     for e in ev:
         e.record()
@@ -424,7 +469,7 @@ def run_trace(args, dev):
         kn = wl.device_normal((T, hkv, d), dtype, dev, 5, step, 1)
         vn = wl.device_normal((T, hkv, d), dtype, dev, 5, step, 2)
         q = wl.device_normal((T, hq, d), dtype, dev, 5, step, 3)
-        scratch.fill_(step & 255)
+        flush(step, stream)
         ev[0].record(stream)
         lib.cb_profile_events(ev[2].cuda_event, ev[3].cuda_event)
         layer.attend(q, kn, vn, stream=stream)
@@ -477,11 +522,128 @@ def run_trace(args, dev):
         "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
         "config": {"workload": "fifo_trace_256req_poisson0.5_lognormal1500_geom256_gqa64/8_d128_bf16",
                    "pool_pages": 200_000, "max_batch_tokens": 2048, "max_requests": 128, "safety_margin": 0.15,
-                   "timing": "each step once, cold (1 GiB written before it); step = device span"},
+                   "timing": f"each step once, cold (1 GiB {'written' if args.flush == 'write' else 'read'} "
+                             "before it); step = device span"},
         "roofline": roof,
         "trace": {"query_tokens": tok, "device_span_s": round(span, 4), "classes": classes,
                   "fragmentation_mean": round(float(np.mean(frag)), 5) if frag else None,
                   "fragmentation_max": round(float(np.max(frag)), 5) if frag else None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def run_sweep(args, dev, w):
+    """Every step of the long-prompt workload that carries a chunk of its
+    20,000-token prompt (40 steps of 512 tokens, the last 32), in order, or,
+    with the chunk workload, the same 40 chunks without the decodes.  Each
+    step runs --warmup untimed and --steps timed times back to back from the
+    same builder state, cold under --cold's rule (by default the steps that move less than
+    1 GB); the step's time is the median device span (append .. combine), its
+    kernel time the median of HIP events around the main attention kernel.  Each step is classed HBM- or MFMA-bound
+    by its algorithmic bytes and flops; the roofline line aggregates the class
+    that holds most of the kernel time."""
+    import numpy as np
+    import torch
+    import chunked_prefill_attention_amd as cb
+    import workloads as wl
+    hq, hkv, d = w.n_q_heads, w.n_kv_heads, w.head_dim
+    esize = 2 if w.dtype == "bf16" else 4
+    t_setup = time.perf_counter()
+    layer, hist = prepare_layer(w, args, dev)
+    lib = cb.load()
+    stream = torch.cuda.current_stream(dev)
+    flush = CacheFlush(args.flush, dev)
+    ev = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
+    for e in sum(ev, []):
+        e.record()
+    log(f"[bench] {w.name} sweep: setup {time.perf_counter() - t_setup:.1f}s")
+    rows = []
+    for k in range(1 << 16):
+        snapshot = layer.builder.clone()
+        desc = layer.schedule().copy()
+        if desc.num_seqs == desc.num_decodes:        # the prompt's last chunk is done
+            break
+        T = desc.num_tokens
+        q = wl.device_normal((T, hq, d), w.dtype, dev, w.seed, 99, 3, k)
+        kn = torch.cat([hist[int(r)][0][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
+        vn = torch.cat([hist[int(r)][1][a:e] for r, a, e in zip(desc.req_ids, desc.q_offsets, desc.context_lens)])
+        out = torch.empty_like(q)
+        nbytes, flops, _, _ = algorithmic(desc, hq, hkv, d, esize, args.window)
+        cold = args.cold == "on" or (args.cold == "auto" and nbytes < 1e9)
+        for r in range(args.warmup + args.steps):       # back to back, as the engine runs steps
+            layer.load_builder(snapshot)
+            layer.schedule(stream=stream)
+            if cold:
+                flush(r, stream)
+            e = ev[r - args.warmup] if r >= args.warmup else None
+            if e:
+                e[0].record(stream)
+                lib.cb_profile_events(e[2].cuda_event, e[3].cuda_event)
+            layer.attend(q, kn, vn, out=out, stream=stream)
+            if e:
+                lib.cb_profile_events(None, None)
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        span = [e[0].elapsed_time(e[1]) / 1e3 for e in ev]
+        kern = [e[2].elapsed_time(e[3]) / 1e3 for e in ev]
+        assert torch.isfinite(out.float()).all(), f"non-finite attention output at step {k}"
+        cls = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+        ks, ss = float(np.median(kern)), float(np.median(span))
+        frac = nbytes / ks / 1e9 / HBM_PEAK_GBS if cls == "hbm" else flops / ks / 1e12 / MFMA_BF16_PEAK_TFLOPS
+        pf = int(desc.num_decodes)                   # the prompt's chunk follows the step's decodes
+        rows.append({"step": k, "query_tokens": T, "decodes": int(desc.num_decodes),
+                     "chunk_offset": int(desc.q_offsets[pf]), "chunk_tokens": int(desc.q_lens[pf]),
+                     "alg_bytes": nbytes, "alg_flops": flops, "class": cls, "cold": int(cold),
+                     "kernel_us": round(ks * 1e6, 2), "span_us": round(ss * 1e6, 2), "kernel_frac": round(frac, 4)})
+        log(f"[bench] step {k}: chunk {rows[-1]['chunk_offset']}+{rows[-1]['chunk_tokens']}, "
+            f"{desc.num_decodes} decodes, kernel {ks * 1e6:.1f} us, span {ss * 1e6:.1f} us, {cls} {frac:.3f}")
+    if args.trace_csv:
+        with open(args.trace_csv, "w") as f:
+            f.write(",".join(rows[0]) + "\n")
+            for r in rows:
+                f.write(",".join(str(v) for v in r.values()) + "\n")
+    classes = {}
+    for c in ("hbm", "mfma"):
+        sel = [r for r in rows if r["class"] == c]
+        if not sel:
+            continue
+        tk = sum(r["kernel_us"] for r in sel) / 1e6
+        b, f = sum(r["alg_bytes"] for r in sel), sum(r["alg_flops"] for r in sel)
+        classes[c] = {"steps": len(sel), "kernel_s": round(tk, 6),
+                      "kernel_frac_of_peak": round((b / tk / 1e9 / HBM_PEAK_GBS) if c == "hbm"
+                                                   else (f / tk / 1e12 / MFMA_BF16_PEAK_TFLOPS), 4),
+                      "kernel_frac_min": min(r["kernel_frac"] for r in sel),
+                      "kernel_frac_max": max(r["kernel_frac"] for r in sel)}
+    top = max(classes, key=lambda c: classes[c]["kernel_s"])
+    sel = [r for r in rows if r["class"] == top]
+    tk = sum(r["kernel_us"] for r in sel) / 1e6
+    if top == "hbm":
+        ach = sum(r["alg_bytes"] for r in sel) / tk / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        ach = sum(r["alg_flops"] for r in sel) / tk / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof.update({"frac": round(ach / roof["peak"], 4), "traffic": None,
+                 "kernel": f"attn_mixed_kernel<{d}, {'true' if args.window > 0 else 'false'}> "
+                           "(the sweep's steps of this class)"})
+    tok = sum(r["query_tokens"] for r in rows)
+    span = sum(r["span_us"] for r in rows) / 1e6
+    log(f"[bench] sweep: {len(rows)} steps, {tok} query tokens, device {span * 1e3:.2f} ms; "
+        + ", ".join(f"{c}: {v['steps']} steps {v['kernel_frac_of_peak']:.3f} of peak" for c, v in classes.items()))
+    rec = {
+        "metric": METRIC, "value": round(tok / span, 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(span / len(rows) * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V; no dataset)",
+        "config": {"workload": w.name.replace("512@19456", "every512") + "_sweep", "steps_swept": len(rows),
+                   "q_heads": hq, "kv_heads": hkv, "head_dim": d, "page_size": 16,
+                   "sliding_window": args.window,
+                   "timing": f"each step --steps times after --warmup untimed runs, enqueued back to back from "
+                             f"the same builder state; steps under 1 GB cold (--cold {args.cold}, 1 GiB {args.flush} before "
+                             f"each run); per step the median device span (append .. combine) and kernel time"},
+        "roofline": roof,
+        "sweep": {"classes": classes, "per_step": rows},
         "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)

@@ -83,7 +83,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 #define CB_DEC_WAVES_PER_SIMD 2
 #endif
 #ifndef CB_DEC_MIN_WAVES     // decode splits: the longest that still gives this many wavefronts
-#define CB_DEC_MIN_WAVES 8192
+#define CB_DEC_MIN_WAVES 6144
 #endif
 #ifndef CB_DEC_MIN_WAVES_ALONE  // ... in a step without prefill work (the decode-only launch)
 #define CB_DEC_MIN_WAVES_ALONE 4096
@@ -1373,7 +1373,7 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   const int64_t max_pages = (max_context_len + 15) / 16;
   const int64_t G = hkv > 0 ? hq / hkv : 1;
   // decode: the longest split (pages per wavefront) that still gives the
-  // decode grid >= 8k wavefronts (about 2-3 rounds of the chip's wave slots),
+  // decode grid >= 6k wavefronts (three rounds of the mixed launch's 2k slots),
   // or >= 4k when no prefill work shares the launch; longer splits write
   // fewer partials for the combine and start fewer wavefronts.  max_pages is
   // the step's longest context, which in a mixed step is usually a prefill

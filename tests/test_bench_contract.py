@@ -56,3 +56,18 @@ def test_windowed_mixed_step_runs():
     assert r.returncode == 0, r.stderr[-2000:]
     rec = json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1])
     assert rec["config"]["sliding_window"] == 1024 and rec["value"] > 0
+
+
+@pytest.mark.gpu
+def test_chunk_sweep_covers_every_chunk_of_the_long_prompt():
+    """--sweep over the chunk workload times the 20,000-token prompt's 40
+    chunks in order (512 tokens each at offsets 0, 512, ..., the last 32)."""
+    r = _bench("--workload", "chunk", "--sweep", "--steps", "1", "--warmup", "0", "--no-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    rec = json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1])
+    rows = rec["sweep"]["per_step"]
+    assert [x["chunk_offset"] for x in rows] == [512 * k for k in range(40)]
+    assert [x["chunk_tokens"] for x in rows] == [512] * 39 + [32]
+    assert all(x["decodes"] == 0 and x["kernel_us"] > 0 for x in rows)
+    assert rec["roofline"]["bound"] == "mfma" and 0 < rec["roofline"]["frac"] <= 1
+    assert rec["config"]["steps_swept"] == 40 and rec["value"] > 0
