@@ -247,6 +247,36 @@ def test_long_decode_splits_d64_and_window(d, window):
     _check_all(st, out, f"long splits d{d} w{window}", window=window)
 
 
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_very_long_contexts_match_oracle(dtype):
+    """Contexts far past the other cases: decodes over 200,000 and 150,001
+    keys (12,500 and 9,376 pages, cut into 196 and 147 splits for the
+    combine to merge) and a 64-token chunk at offset 131,072 (its 512
+    GQA-packed rows in four row tiles, each cut into ~100 key ranges).  Every
+    head of every decode row and of the chunk's first, second, middle and
+    last rows against the row-by-row oracle.  Queries are drawn with std 4,
+    so that a few keys anywhere in the context carry most of a row's weight
+    (the heaviest 1,024-key stretch of a decode row holds ~0.3 of it): a
+    dropped, repeated or misplaced split moves the output well past the
+    tolerance."""
+    seqs = [(200_000, 1), (150_001, 1), (131_072 + 64, 64)]
+    hq = 16
+    say(f"very long contexts {dtype}")
+    st = Step(seqs, hq, 2, 128, dtype, seed=31, q_std=4.0)
+    kc, vc = st.upload()
+    out = st.run(kc, vc)
+    for s, (c, n) in enumerate(seqs):
+        rows = [(i, h) for i in sorted({0, min(1, n - 1), n // 2, n - 1}) for h in range(hq)]
+        ii = [i for i, _ in rows]
+        hh = [h for _, h in rows]
+        ref = ora.attend_rows(st.q[s], st.k_hist[s], st.v_hist[s], st.scale, rows=rows)[ii, hh]
+        am = ora.attend_rows(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale,
+                             rows=rows)[ii, hh] if dtype == "bf16" else None
+        err = compare(st.out_rows(out, s)[ii, hh], ref, dtype, f"seq {s} (ctx {c}, q {n})", am)
+        say(f"  seq {s}: ctx {c}, {len(rows)} rows, max abs err {err:.2e}")
+
+
 def test_bad_page_ids_do_not_fault():
     """Out-of-range block-table entries (a broken precondition) must not fault:
     they read page 0, so with finite cache contents the output stays finite."""
