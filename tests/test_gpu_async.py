@@ -8,7 +8,9 @@ kernel -- has not run yet.  Here ten distinct steps are enqueued back to back
 behind a device backlog (after one warm-up step), with no host synchronisation
 between them, each into
 its own output buffer; the engine must report that a schedule waited for a
-slot, and every step's output is then compared with the oracle.
+slot, and every step's output is then compared with the oracle.  The same
+runs with graph replay ([CBA] "CUDA graphs"): padded step shapes recorded
+and replayed on the layer's stream while earlier steps are still pending.
 """
 import time
 
@@ -25,7 +27,8 @@ import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def test_overlapped_engine_steps_match_the_oracle():
+@pytest.mark.parametrize("graphs", [(0, 0), (64, 1024)], ids=["direct", "graphs"])
+def test_overlapped_engine_steps_match_the_oracle(graphs):
     hq, hkv, d, seed = 32, 8, 128, 41
     budget, max_req = 640, 64
     # 24 decodes (contexts 1,500 .. 4,000) and two prompts of 1,500 and 2,600
@@ -35,7 +38,7 @@ def test_overlapped_engine_steps_match_the_oracle():
     reqs = [(int(c) - 1, 40, int(c) - 1) for c in ctx] + [(1500, 4, 0), (2600, 4, 0)]
     pool = sum(-(-(p + o) // 16) for p, o, _ in reqs) + 64
     L = PagedAttentionLayer(hq, hkv, d, pool, budget, max_req, "bf16", page_shuffle_seed=seed,
-                            cache_fill=float("nan"))
+                            cache_fill=float("nan"), graph_q_interval=graphs[0], graph_kv_interval=graphs[1])
     hist = {}
     for i, (p, o, c) in enumerate(reqs):
         L.builder.submit(i, p, o, c)
@@ -84,6 +87,8 @@ def test_overlapped_engine_steps_match_the_oracle():
         f"all drained {1e3 * (time.perf_counter() - t0):.1f} ms after the first enqueue")
     assert stats["steps_attended"] == n_steps + 1
     assert stats["slot_waits"] >= 1, "no schedule had to wait: the steps did not overlap"
+    if graphs[0]:
+        assert stats["graph_replays"] == n_steps + 1 and stats["graph_captures"] >= 1
 
     scale = wl.softmax_scale(d)
     host = {i: (k.float().cpu().numpy(), v.float().cpu().numpy()) for i, (k, v) in hist.items()}
