@@ -248,12 +248,15 @@ def test_long_decode_splits_d64_and_window(d, window):
 
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_very_long_contexts_match_oracle(dtype):
+@pytest.mark.parametrize("dtype,d,hq,hkv,window", [("bf16", 128, 16, 2, 0), ("f32", 128, 16, 2, 0),
+                                                   ("bf16", 64, 4, 4, 0), ("bf16", 128, 16, 2, 5000)])
+def test_very_long_contexts_match_oracle(dtype, d, hq, hkv, window):
     """Contexts far past the other cases: decodes over 200,000 and 150,001
     keys (12,500 and 9,376 pages, cut into 196 and 147 splits for the
-    combine to merge) and a 64-token chunk at offset 131,072 (its 512
-    GQA-packed rows in four row tiles, each cut into ~100 key ranges).  Every
+    combine to merge) and a 64-token chunk at offset 131,072 (its GQA-packed
+    rows in row tiles each cut into ~100 key ranges); at D 128 with eight
+    query heads per KV head, at D 64 with one, and under a 5,000-token
+    sliding window (the splits then cover only the window's pages).  Every
     head of every decode row and of the chunk's first, second, middle and
     last rows against the row-by-row oracle.  Queries are drawn with std 4,
     so that a few keys anywhere in the context carry most of a row's weight
@@ -261,21 +264,22 @@ def test_very_long_contexts_match_oracle(dtype):
     dropped, repeated or misplaced split moves the output well past the
     tolerance."""
     seqs = [(200_000, 1), (150_001, 1), (131_072 + 64, 64)]
-    hq = 16
-    say(f"very long contexts {dtype}")
-    st = Step(seqs, hq, 2, 128, dtype, seed=31, q_std=4.0)
+    say(f"very long contexts {dtype} d{d} {hq}/{hkv} window {window}")
+    st = Step(seqs, hq, hkv, d, dtype, seed=31 + d + window, q_std=4.0)
     kc, vc = st.upload()
-    out = st.run(kc, vc)
+    q = to_dev(np.concatenate(st.q), dtype)
+    out = cb.attention_step(q, kc, vc, i32(st.bt), i32(st.qsl), i32(st.ctx), i32(st.off), st.num_decodes,
+                            st.max_ctx, st.scale, sliding_window=window)
+    torch.cuda.synchronize()
     for s, (c, n) in enumerate(seqs):
         rows = [(i, h) for i in sorted({0, min(1, n - 1), n // 2, n - 1}) for h in range(hq)]
         ii = [i for i, _ in rows]
         hh = [h for _, h in rows]
-        ref = ora.attend_rows(st.q[s], st.k_hist[s], st.v_hist[s], st.scale, rows=rows)[ii, hh]
-        am = ora.attend_rows(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale,
-                             rows=rows)[ii, hh] if dtype == "bf16" else None
+        ref = ora.attend_rows(st.q[s], st.k_hist[s], st.v_hist[s], st.scale, rows=rows, window=window)[ii, hh]
+        am = ora.attend_rows(st.q[s], st.k_hist[s], np.abs(st.v_hist[s]), st.scale, rows=rows,
+                             window=window)[ii, hh] if dtype == "bf16" else None
         err = compare(st.out_rows(out, s)[ii, hh], ref, dtype, f"seq {s} (ctx {c}, q {n})", am)
         say(f"  seq {s}: ctx {c}, {len(rows)} rows, max abs err {err:.2e}")
-
 
 def test_bad_page_ids_do_not_fault():
     """Out-of-range block-table entries (a broken precondition) must not fault:
