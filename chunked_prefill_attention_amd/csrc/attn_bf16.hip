@@ -29,8 +29,9 @@
 //    Tiles wholly above the diagonal are never loaded.  Long key ranges are
 //    cut into several items so that a long chunk spreads over every CU.
 //
-// Items with more than one split write unnormalised partial results (row
-// max, row sum, O); the combine kernel merges them by log-sum-exp.
+// Items with more than one split write partial results (row max, row sum,
+// and O divided by that sum, in fp16); the combine kernel merges them by
+// log-sum-exp.
 //
 // Block order: the work lists start with the live item counts; live blocks
 // run first (prefill first when its workgroups fit in one round of the
@@ -50,7 +51,8 @@
 // in raw units; exponentials are exp2(s*scale*log2(e) - m*scale*log2(e)) with
 // one FMA), probabilities rounded to bf16 for the P V product (and, in
 // prefill, for the row sum, so numerator and normaliser weigh the same
-// values), output rounded to bf16 (round to nearest even).  The running max
+// values), output rounded to bf16 (round to nearest even); split-K partial
+// outputs are kept in fp16 divided by their own sum.  The running max
 // is raised only when a score exceeds it by more than 8 in log2 units, so
 // the accumulator rescale is usually skipped; weights stay <= 2^8.  Cache slots at or past the context length are masked by
 // select and their V entries zeroed (in prefill, as they are read from LDS),
@@ -147,9 +149,9 @@ struct Params {
   int32_t* dec_first;    // [num_decodes] first full-length decode item of each sequence
   int32_t* dec_rem;      // [num_decodes] the sequence's shorter last item, or -1
   float2* dec_ml;        // [decode wave][G] (running max in raw score units, sum)
-  float* dec_o;          // [decode wave][G][D] unnormalised
+  uint16_t* dec_o;       // [decode wave][G][D] fp16, divided by the split's own sum
   float2* pf_ml;         // [prefill item][PF_ROWS]
-  float* pf_o;           // [prefill item][PF_ROWS][D]
+  uint16_t* pf_o;        // [prefill item][PF_ROWS][D] fp16, divided by the split's own sum
   int32_t bt_stride;
   const int32_t* bt_off;  // row offsets of packed block tables, or null (row s at s * bt_stride)
   int32_t num_seqs, num_decodes;
@@ -195,6 +197,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, b16x2));
+}
+
+// Split-K partial outputs are stored as fp16 after division by the split's
+// own sum: a weighted mean of V rows, so |value| <= max |v| and fp16's
+// 11-bit significand keeps it to 2^-11 relative (four times finer than the
+// bf16 output), in half the bytes of fp32.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+__device__ __forceinline__ float4 unpack_f16x4(uint2 v) {
+  const f16x2 a = __builtin_bit_cast(f16x2, v.x), b = __builtin_bit_cast(f16x2, v.y);
+  return make_float4((float)a[0], (float)a[1], (float)b[0], (float)b[1]);
 }
 
 // acc + the sum of eight bf16 values (four packed pairs), one dot2 with (1, 1) per pair
@@ -674,9 +690,12 @@ __device__ __forceinline__ void decode_wave(const Params& p, int w) {
     }
   } else {
     const size_t prow = (size_t)w * G + hl;
-    float* po = p.dec_o + prow * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* po = p.dec_o + prow * D;
 #pragma unroll
-    for (int tt = 0; tt < D / 16; ++tt) *reinterpret_cast<floatx4*>(po + 16 * tt + 4 * g) = o[tt];
+    for (int tt = 0; tt < D / 16; ++tt)
+      *reinterpret_cast<uint2*>(po + 16 * tt + 4 * g) = make_uint2(pack_f16x2(o[tt][0] * inv, o[tt][1] * inv),
+                                                                   pack_f16x2(o[tt][2] * inv, o[tt][3] * inv));
     if (g == 0) p.dec_ml[prow] = make_float2(m, l);
   }
 }
@@ -1037,13 +1056,15 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int b) {
       }
   } else {
     const size_t prow = ((size_t)slot * p.hkv + kvh) * PF_ROWS + wv * 32 + l32;
-    float* po = p.pf_o + prow * D;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // 0: every key of this range is above the row's diagonal
+    uint16_t* po = p.pf_o + prow * D;
 #pragma unroll
     for (int dt = 0; dt < NO; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<floatx4*>(po + 32 * dt + 8 * q4 + 4 * gg) =
-            floatx4{o[dt][4 * q4 + 0], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]};
+        *reinterpret_cast<uint2*>(po + 32 * dt + 8 * q4 + 4 * gg) =
+            make_uint2(pack_f16x2(o[dt][4 * q4 + 0] * inv, o[dt][4 * q4 + 1] * inv),
+                       pack_f16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv));
     if (gg == 0) p.pf_ml[prow] = make_float2(m, lt);
   }
 }
@@ -1171,33 +1192,44 @@ __device__ void combine_decode(const Params& p, int wave) {
     lsum += fast_exp2((ml.x - M) * c) * ml.y;
   }
   for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+  // lane l merges output dims E*l .. E*l + E-1 (one 4-byte fp16 pair at D 128)
+  static_assert(E == 1 || E == 2, "D 64 or 128");
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   constexpr int U = 8;
   for (int i0 = 0; i0 < nsplit; i0 += U) {
-    float mu[U], val[U][E];
+    float2 ml[U];
+    float val[U][E];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u;
       const size_t prow = ((size_t)item_of(min(i, nsplit - 1)) * p.hkv + kvh) * G + hl;
-      mu[u] = i < nsplit ? p.dec_ml[prow].x : -INFINITY;
-#pragma unroll
-      for (int e = 0; e < E; ++e) val[u][e] = p.dec_o[prow * D + lane + 64 * e];
+      ml[u] = p.dec_ml[prow];
+      if (i >= nsplit) ml[u].x = -INFINITY;
+      const uint16_t* po = p.dec_o + prow * D + E * lane;
+      if constexpr (E == 2) {
+        const f16x2 h2 = __builtin_bit_cast(f16x2, *reinterpret_cast<const uint32_t*>(po));
+        val[u][0] = (float)h2[0];
+        val[u][1] = (float)h2[1];
+      } else {
+        val[u][0] = (float)__builtin_bit_cast(_Float16, *po);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float w = fast_exp2((mu[u] - M) * c);
+      // the split's weight: its sum, rescaled to the common maximum
+      const float w = fast_exp2((ml[u].x - M) * c) * ml[u].y;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(w, val[u][e], acc[e]);
     }
   }
   const float inv = 1.f / lsum;
-  uint16_t* orow = p.out + ((size_t)p.qsl[s] * p.hq + h) * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const __bf16 v = (__bf16)(acc[e] * inv);
-    orow[lane + 64 * e] = __builtin_bit_cast(uint16_t, v);
+  uint16_t* orow = p.out + ((size_t)p.qsl[s] * p.hq + h) * D + E * lane;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+    *orow = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
   }
 }
 
@@ -1234,11 +1266,16 @@ __device__ void combine_prefill(const Params& p, int gb) {
   for (int i = 0; i < nsplit; ++i) {
     const size_t prow = ((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl;
     const float2 ml = p.pf_ml[prow];
-    const float w = ml.x == -INFINITY ? 0.f : fast_exp2((ml.x - M) * c);
-    lsum = fmaf(w, ml.y, lsum);
-    const floatx4* po = reinterpret_cast<const floatx4*>(p.pf_o + prow * D + dc);
+    // the split's weight: its sum, rescaled to the common maximum (0 when
+    // every key of the range was above the row's diagonal)
+    const float w = ml.x == -INFINITY ? 0.f : fast_exp2((ml.x - M) * c) * ml.y;
+    lsum += w;
+    const uint2* po = reinterpret_cast<const uint2*>(p.pf_o + prow * D + dc);
 #pragma unroll
-    for (int e = 0; e < E / 4; ++e) acc[e] += w * po[e];
+    for (int e = 0; e < E / 4; ++e) {
+      const float4 v = unpack_f16x4(po[e]);
+      acc[e] += w * floatx4{v.x, v.y, v.z, v.w};
+    }
   }
   const float inv = 1.f / lsum;
   const int qi = row / G, hh = row - qi * G;
@@ -1278,9 +1315,9 @@ hipError_t launch_d(const AttnArgs& a, const Bf16Plan& pl, const WorkLists* list
   p.dec_first = reinterpret_cast<int32_t*>(ws + pl.off_dec_first);
   p.dec_rem = reinterpret_cast<int32_t*>(ws + pl.off_dec_rem);
   p.dec_ml = reinterpret_cast<float2*>(ws + pl.off_dec_ml);
-  p.dec_o = reinterpret_cast<float*>(ws + pl.off_dec_o);
+  p.dec_o = reinterpret_cast<uint16_t*>(ws + pl.off_dec_o);
   p.pf_ml = reinterpret_cast<float2*>(ws + pl.off_pf_ml);
-  p.pf_o = reinterpret_cast<float*>(ws + pl.off_pf_o);
+  p.pf_o = reinterpret_cast<uint16_t*>(ws + pl.off_pf_o);
   p.bt_stride = a.bt_stride;
   p.bt_off = a.bt_offsets;
   p.num_seqs = a.num_seqs;
@@ -1429,10 +1466,10 @@ Bf16Plan plan_bf16(int32_t num_seqs, int32_t num_decodes, int32_t num_tokens, in
   pl.off_dec_rem = off;     off = align(off + (size_t)num_decodes * sizeof(int32_t));
   const size_t drows = (size_t)pl.dec_cap * hkv * G;
   pl.off_dec_ml = off;      off = align(off + drows * 8);
-  pl.off_dec_o = off;       off = align(off + drows * head_dim * sizeof(float));
+  pl.off_dec_o = off;       off = align(off + drows * head_dim * sizeof(uint16_t));
   const size_t prows = pl.pf_may_split ? (size_t)pl.pf_item_cap * hkv * PF_ROWS : 0;
   pl.off_pf_ml = off;       off = align(off + prows * 8);
-  pl.off_pf_o = off;        off = align(off + prows * head_dim * sizeof(float));
+  pl.off_pf_o = off;        off = align(off + prows * head_dim * sizeof(uint16_t));
   pl.bytes = off;
   return pl;
 }
