@@ -50,36 +50,56 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
   constexpr int ROWB = D * ES;        // bytes of one token row of one head
   constexpr int CH = ROWB / 16;       // 16-byte chunks per row
   constexpr int LROW = ROWB + 16;     // padded LDS row (spreads the column reads over banks)
+  constexpr int NE = (16 * CH + 255) / 256;  // row chunks per thread
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[16 * LROW];
+  __shared__ int32_t sslot[16];       // the group's slots (-1: not written)
 
   const int tid = threadIdx.x;
   const int h = blockIdx.x % hkv;
   const int t0 = (blockIdx.x / hkv) * 16;
   const int64_t slot_limit = (int64_t)num_pages * 16;
 
-  for (int e = tid; e < 16 * CH; e += 256) {
-    const int r = e / CH, c = e % CH;
-    const int t = t0 + r;
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (t < num_tokens) {
-      const size_t src = ((size_t)t * hkv + h) * ROWB + c * 16;
-      vv = *reinterpret_cast<const uint4*>(v_new + src);
-      const int32_t slot = slots[t];
-      if (slot >= 0 && slot < slot_limit) {
-        kv = *reinterpret_cast<const uint4*>(k_new + src);
-        const size_t dst = (((size_t)(slot >> 4) * hkv + h) * 16 + (slot & 15)) * ROWB + c * 16;
-        *reinterpret_cast<uint4*>(k_cache + dst) = kv;
+  // The slot mapping may live in mapped host memory (the engine's staging
+  // slot): it is read once per group, here, and shared through LDS.
+  if (tid < 16) {
+    const int t = t0 + tid;
+    int32_t sl = t < num_tokens ? slots[t] : -1;
+    sslot[tid] = (sl >= 0 && sl < slot_limit) ? sl : -1;
+  }
+  uint4 kreg[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = tid + 256 * i;
+    kreg[i] = make_uint4(0, 0, 0, 0);
+    if (e < 16 * CH) {
+      const int r = e / CH, c = e % CH;
+      const int t = t0 + r;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (t < num_tokens) {
+        const size_t src = ((size_t)t * hkv + h) * ROWB + c * 16;
+        vv = *reinterpret_cast<const uint4*>(v_new + src);
+        kreg[i] = *reinterpret_cast<const uint4*>(k_new + src);
       }
+      *reinterpret_cast<uint4*>(vbuf + r * LROW + c * 16) = vv;
     }
-    *reinterpret_cast<uint4*>(vbuf + r * LROW + c * 16) = vv;
   }
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NE; ++i) {
+    const int e = tid + 256 * i;
+    if (e < 16 * CH) {
+      const int r = e / CH, c = e % CH;
+      const int32_t slot = sslot[r];
+      if (slot >= 0) {
+        const size_t dst = (((size_t)(slot >> 4) * hkv + h) * 16 + (slot & 15)) * ROWB + c * 16;
+        *reinterpret_cast<uint4*>(k_cache + dst) = kreg[i];
+      }
+    }
+  }
   for (int e = tid; e < 16 * D; e += 256) {
     const int r = e & 15, d = e >> 4;
-    const int t = t0 + r;
-    if (t >= num_tokens) continue;
-    const int32_t slot = slots[t];
-    if (slot < 0 || slot >= slot_limit) continue;
+    const int32_t slot = sslot[r];
+    if (slot < 0) continue;
     const size_t dst = ((((size_t)(slot >> 4) * hkv + h) * D + d) * 16 + (slot & 15)) * ES;
     if constexpr (ES == 2) {
       *reinterpret_cast<uint16_t*>(v_cache + dst) = *reinterpret_cast<const uint16_t*>(vbuf + r * LROW + d * 2);
