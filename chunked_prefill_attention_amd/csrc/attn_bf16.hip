@@ -1183,31 +1183,14 @@ __device__ void combine_decode(const Params& p, int wave) {
   // split i lives at item j0 + i (full splits) or jr (the short last split)
   auto item_of = [&](int i) { return i < nfull ? j0 + i : jr; };
   const float c = p.scale_log2;
-  float M = -INFINITY;
-  for (int i = lane; i < nsplit; i += 64) M = fmaxf(M, p.dec_ml[((size_t)item_of(i) * p.hkv + kvh) * G + hl].x);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float lsum = 0.f;
-  for (int i = lane; i < nsplit; i += 64) {
-    const float2 ml = p.dec_ml[((size_t)item_of(i) * p.hkv + kvh) * G + hl];
-    lsum += fast_exp2((ml.x - M) * c) * ml.y;
-  }
-  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
   // lane l merges output dims E*l .. E*l + E-1 (one 4-byte fp16 pair at D 128)
   static_assert(E == 1 || E == 2, "D 64 or 128");
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  constexpr int U = 8;
-  for (int i0 = 0; i0 < nsplit; i0 += U) {
-    float2 ml[U];
-    float val[U][E];
+  constexpr int U = 8;  // splits whose values are loaded together
+  auto prow_of = [&](int i) { return ((size_t)item_of(min(i, nsplit - 1)) * p.hkv + kvh) * G + hl; };
+  auto load_vals = [&](int i0, float (&val)[U][E]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u;
-      const size_t prow = ((size_t)item_of(min(i, nsplit - 1)) * p.hkv + kvh) * G + hl;
-      ml[u] = p.dec_ml[prow];
-      if (i >= nsplit) ml[u].x = -INFINITY;
-      const uint16_t* po = p.dec_o + prow * D + E * lane;
+      const uint16_t* po = p.dec_o + prow_of(i0 + u) * D + E * lane;
       if constexpr (E == 2) {
         const f16x2 h2 = __builtin_bit_cast(f16x2, *reinterpret_cast<const uint32_t*>(po));
         val[u][0] = (float)h2[0];
@@ -1216,10 +1199,51 @@ __device__ void combine_decode(const Params& p, int wave) {
         val[u][0] = (float)__builtin_bit_cast(_Float16, *po);
       }
     }
+  };
+  // the first splits' values are in flight while the weights are formed
+  float val[U][E];
+  load_vals(0, val);
+  // split i's weight is its sum rescaled to the common maximum M; up to 128
+  // splits the weights stay in two registers per lane (splits l and l + 64)
+  // and the loop below takes them with readlane, with no second load
+  const bool few = nsplit <= 128;
+  float M = -INFINITY, lsum = 0.f, w0 = 0.f, w1 = 0.f;
+  if (few) {
+    const float2 a = lane < nsplit ? p.dec_ml[prow_of(lane)] : make_float2(-INFINITY, 0.f);
+    const float2 b = lane + 64 < nsplit ? p.dec_ml[prow_of(lane + 64)] : make_float2(-INFINITY, 0.f);
+    M = fmaxf(a.x, b.x);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    w0 = lane < nsplit ? fast_exp2((a.x - M) * c) * a.y : 0.f;
+    w1 = lane + 64 < nsplit ? fast_exp2((b.x - M) * c) * b.y : 0.f;
+    lsum = w0 + w1;
+  } else {
+    for (int i = lane; i < nsplit; i += 64) M = fmaxf(M, p.dec_ml[prow_of(i)].x);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    for (int i = lane; i < nsplit; i += 64) {
+      const float2 ml = p.dec_ml[prow_of(i)];
+      lsum += fast_exp2((ml.x - M) * c) * ml.y;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int i0 = 0; i0 < nsplit; i0 += U) {
+    if (i0 > 0) load_vals(i0, val);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // the split's weight: its sum, rescaled to the common maximum
-      const float w = fast_exp2((ml[u].x - M) * c) * ml[u].y;
+      const int i = i0 + u;
+      float w;
+      if (few) {
+        const int li = i & 63;
+        const float wa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w0), li));
+        const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w1), li));
+        w = i < 64 ? wa : wb;
+      } else {
+        const float2 ml = p.dec_ml[prow_of(i)];
+        w = fast_exp2((ml.x - M) * c) * ml.y;
+      }
+      w = i < nsplit ? w : 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] = fmaf(w, val[u][e], acc[e]);
     }
