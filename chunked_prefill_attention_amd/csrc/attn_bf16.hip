@@ -1280,26 +1280,61 @@ __device__ void combine_prefill(const Params& p, int gb) {
   const int row = tile * PF_ROWS + rl;
   if (row >= R) return;
   const float c = p.scale_log2;
-  float M = -INFINITY;
-  for (int i = 0; i < nsplit; ++i)
-    M = fmaxf(M, p.pf_ml[((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl].x);
-  float lsum = 0.f;
+  // Splits are merged in groups of U with a running maximum; the next
+  // group's loads are in flight while one group is merged, so a long list of
+  // splits costs about one memory round trip per group, a short one one.
+  constexpr int U = 4;
+  struct Group {
+    float2 ml[U];
+    uint2 v[U][E / 4];
+  };
+  auto load = [&](int i0, Group& g) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < nsplit) {  // the same for the whole workgroup
+        const size_t prow = ((size_t)(first + i0 + u) * p.hkv + kvh) * PF_ROWS + rl;
+        g.ml[u] = p.pf_ml[prow];
+        const uint2* po = reinterpret_cast<const uint2*>(p.pf_o + prow * D + dc);
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e) g.v[u][e] = po[e];
+      } else {
+        g.ml[u] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int e = 0; e < E / 4; ++e) g.v[u][e] = make_uint2(0, 0);
+      }
+    }
+  };
+  float M = -INFINITY, lsum = 0.f;
   floatx4 acc[E / 4];
 #pragma unroll
   for (int e = 0; e < E / 4; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < nsplit; ++i) {
-    const size_t prow = ((size_t)(first + i) * p.hkv + kvh) * PF_ROWS + rl;
-    const float2 ml = p.pf_ml[prow];
-    // the split's weight: its sum, rescaled to the common maximum (0 when
-    // every key of the range was above the row's diagonal)
-    const float w = ml.x == -INFINITY ? 0.f : fast_exp2((ml.x - M) * c) * ml.y;
-    lsum += w;
-    const uint2* po = reinterpret_cast<const uint2*>(p.pf_o + prow * D + dc);
+  Group cur, nxt;
+  load(0, cur);
+  for (int i0 = 0; i0 < nsplit; i0 += U) {
+    if (i0 + U < nsplit) load(i0 + U, nxt);
+    float gm = M;
 #pragma unroll
-    for (int e = 0; e < E / 4; ++e) {
-      const float4 v = unpack_f16x4(po[e]);
-      acc[e] += w * floatx4{v.x, v.y, v.z, v.w};
+    for (int u = 0; u < U; ++u) gm = fmaxf(gm, cur.ml[u].x);
+    // a larger maximum rescales what is merged so far (nothing while M = -inf)
+    const float r = M == -INFINITY ? 0.f : fast_exp2((M - gm) * c);
+    lsum *= r;
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e) acc[e] *= r;
+    M = gm;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // the split's weight: its sum, rescaled to the running maximum (0 when
+      // every key of the range was above the row's diagonal, or past the list)
+      const float2 ml = cur.ml[u];
+      const float w = ml.x == -INFINITY ? 0.f : fast_exp2((ml.x - M) * c) * ml.y;
+      lsum += w;
+#pragma unroll
+      for (int e = 0; e < E / 4; ++e) {
+        const float4 v = unpack_f16x4(cur.v[u][e]);
+        acc[e] += w * floatx4{v.x, v.y, v.z, v.w};
+      }
     }
+    cur = nxt;
   }
   const float inv = 1.f / lsum;
   const int qi = row / G, hh = row - qi * G;
