@@ -1334,7 +1334,7 @@ __device__ void combine_prefill(const Params& p, int gb) {
         acc[e] += w * floatx4{v.x, v.y, v.z, v.w};
       }
     }
-    cur = nxt;
+    if (i0 + U < nsplit) cur = nxt;
   }
   const float inv = 1.f / lsum;
   const int qi = row / G, hh = row - qi * G;
