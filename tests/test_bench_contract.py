@@ -71,3 +71,9 @@ def test_chunk_sweep_covers_every_chunk_of_the_long_prompt():
     assert all(x["decodes"] == 0 and x["kernel_us"] > 0 for x in rows)
     assert rec["roofline"]["bound"] == "mfma" and 0 < rec["roofline"]["frac"] <= 1
     assert rec["config"]["steps_swept"] == 40 and rec["value"] > 0
+
+
+def test_sweep_applies_to_the_long_prompt_workloads_only():
+    r = _bench("--workload", "mixed", "--sweep", timeout=300)
+    assert r.returncode != 0
+    assert "--sweep applies to the long and chunk workloads" in (r.stderr + r.stdout)
